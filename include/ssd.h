@@ -1,0 +1,219 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) batched lossless verify-and-resample
+ * library for Speculative Speculative Decoding (SSD) and its Saguaro pieces.
+ *
+ * Sources, cited by page title and section (the pages carry no code and all
+ * of their formulas were lost in extraction; the readings are stated at each
+ * call):
+ *   [SSD-A] "全球最強推理引擎還快2倍，斯坦福、普林斯頓破解大模型串行魔咒" (repost of a
+ *           機器之心 article), section "SSD 如何實現草擬與驗證并行？".
+ *   [SSD-B] "超越传统SD：SSD框架全异步解码实现4.7倍平均加速", sections
+ *           "投机解码的瓶颈与 SSD 的核心机制" and "Saguaro 算法：解决异步推测的三大挑战"
+ *           (parts "1. 验证结果预测与缓存拓扑优化", "2. 操纵残差分布",
+ *           "3. 大 Batch 下的退避策略").
+ *   Acceptance rule and residual: the textbook speculative-sampling rule
+ *   (Leviathan, Kalman, Matias, ICML 2023), which [SSD-A] describes in words.
+ *   Random numbers: Philox4x32-10 (Salmon et al., "Parallel Random Numbers:
+ *   As Easy as 1, 2, 3", SC'11).
+ *
+ * Common conventions
+ * ------------------
+ * - Logits are row-major, vocabulary contiguous: row r starts at element
+ *   r * ld.  Sample/verify tensors are [B, K+1, V] rows (row = b*(K+1) + j).
+ *   Entries must be finite or -inf (weight zero); each row needs one finite
+ *   entry.  NaN and +inf are not supported.
+ * - Pointers named "device" are HIP device memory owned by the caller; the
+ *   library allocates nothing and keeps no state between calls.
+ * - `stream` is a hipStream_t (NULL = default stream).  Every call is
+ *   asynchronous: it validates its scalar arguments, enqueues its kernels
+ *   and returns; nothing synchronises inside the library.
+ * - Errors: argument checks run on the host before any launch and return
+ *   SSD_ERR_INVALID_ARG / SSD_ERR_UNSUPPORTED / SSD_ERR_WORKSPACE without
+ *   enqueuing anything; a failed launch returns SSD_ERR_HIP.  No call aborts
+ *   or throws.  Values that live in device memory (temperatures, token ids,
+ *   accepted lengths, depth offsets) cannot be checked on the host; the
+ *   kernels guard every index they derive from them (see each call).
+ * - Temperatures: one per row (softmax_t) or per sequence (sample, verify).
+ *   A temperature that is not > 0 selects the greedy path (argmax, no
+ *   randomness).
+ * - Ties (argmax, top-F order, Gumbel scores) go to the lowest index.
+ * - Workspace: a device buffer of at least ssd_workspace_bytes(...) bytes,
+ *   16-byte aligned, ZERO-FILLED before its first use.  Each call leaves its
+ *   internal counters at zero again, so the buffer can be reused by later
+ *   calls of the same op without clearing.  Calls that share a workspace
+ *   must not overlap in time (use one stream or one workspace per stream).
+ * - Randomness: key = (seed & 0xffffffff, seed >> 32); counter =
+ *   (idx >> 2, b, j, stream id); the draw is output word idx & 3, with idx the
+ *   token id (token streams), the 2048-token block id (block streams) or 0
+ *   (acceptance).  Stream ids: 0 draft token, 1 draft block, 2 acceptance,
+ *   3 bonus token, 4 bonus block, 5 miss fallback.  Uniform u = ((w >> 9) +
+ *   0.5) * 2^-23; Gumbel g = -ln(-ln u).
+ * - Sampling from weights w uses the exact two-level Gumbel-max rule over
+ *   2048-token blocks: block beta* = argmax ln W_beta + g(beta) over blocks of
+ *   nonzero mass, then token = argmax ln w_x + g(x) inside beta*.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_BLOCK 2048         /* vocabulary block of the two-level sampler */
+#define SSD_MAX_V (1 << 20)    /* largest vocabulary */
+#define SSD_MAX_K 32           /* largest number of drafted tokens */
+#define SSD_MAX_F 64           /* largest top-F */
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1, /* null pointer, size out of range, bad C, ... */
+  SSD_ERR_UNSUPPORTED = 2, /* valid request this build does not handle   */
+  SSD_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned */
+  SSD_ERR_HIP = 4          /* a HIP launch failed                        */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 } ssd_dtype;
+
+typedef enum {
+  SSD_OP_SOFTMAX_T = 0,
+  SSD_OP_TOPF = 1,
+  SSD_OP_SAMPLE = 2,
+  SSD_OP_VERIFY = 3
+} ssd_op;
+
+/* Per-row statistics (16 bytes).  max = largest logit; argmax = its lowest
+ * index; lse = ln sum_x w_x relative to max, i.e. the row's normaliser in
+ * nats with w_x = exp((z_x - max)/T) (times C on the top-F set for draft rows
+ * of ssd_saguaro_sample).  Greedy rows have lse = 0. */
+typedef struct {
+  double lse;
+  float max;
+  int32_t argmax;
+} ssd_row_stats;
+
+/* Temperature softmax row statistics ([SSD-A] and [SSD-B] part 2 name the
+ * sampling temperature; p = softmax(z / T)).
+ *   logits      device [rows, ld] of dtype dt, V <= ld
+ *   temperature device float [rows]
+ *   out_stats   device ssd_row_stats [rows]
+ *   out_probs   device float [rows, V] (dense, row stride V) or NULL; greedy
+ *               rows get onehot(argmax).
+ *   workspace   ssd_workspace_bytes(SSD_OP_SOFTMAX_T, rows, 0, V) bytes.
+ * Errors: rows < 1, V < 1, V > SSD_MAX_V, ld < V, null pointers. */
+ssd_status ssd_softmax_t(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, int64_t ld,
+                         const float* temperature, ssd_row_stats* out_stats, float* out_probs,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Top-F of the raw logits of each row, ordered by value descending then index
+ * ascending ([SSD-A]: the bonus token is predicted from the draft's most
+ * likely logits).
+ *   out_idx device int32 [rows, F]; out_val device float [rows, F] (the exact
+ *   logits) or NULL.  1 <= F <= min(SSD_MAX_F, V).
+ *   workspace   ssd_workspace_bytes(SSD_OP_TOPF, rows, 0, V) bytes. */
+ssd_status ssd_topf(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, int64_t ld, int32_t F,
+                    int32_t* out_idx, float* out_val, void* workspace, size_t ws_bytes, void* stream);
+
+/* Draft side of one SSD round with Saguaro sampling sigma_{F,C} ([SSD-B] part
+ * 2: the draft's most likely tokens are sampled less often so that the
+ * residual mass, and with it the bonus token, lands in the cached set).
+ * Reading of the lost formula: with S = top-F raw draft logits of the row,
+ * w_x = C * q_x on S and q_x elsewhere, sigma = w / sum w, q = softmax(z/T).
+ *   draft_logits device [B, K+1, ld] rows of dtype dt
+ *   temperature  device float [B]
+ *   F            size of S, 0 <= F <= min(SSD_MAX_F, V); C in (0, 1]
+ *   F_out        entries of out_topf per row, F <= F_out <= min(SSD_MAX_F, V)
+ *                (0 allowed when F = 0); the first F of them are S
+ *   seed         Philox key
+ * Outputs (device):
+ *   out_tokens   int32 [B, K]: x_j ~ sigma_j for j < K (greedy: argmax)
+ *   out_q        float [B, K]: sigma_j(x_j) (greedy: 1)
+ *   out_stats    ssd_row_stats [B, K+1]: lse = ln sum w relative to max
+ *   out_topf_idx int32 [B, K+1, F_out] or NULL when F_out = 0
+ *   out_topf_val float [B, K+1, F_out] or NULL
+ * Row K is not sampled; its stats and top-F predict the bonus after K
+ * acceptances.  workspace: ssd_workspace_bytes(SSD_OP_SAMPLE, B, K, V). */
+ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K, int64_t V,
+                              int64_t ld, const float* temperature, int32_t F, float C, int32_t F_out,
+                              uint64_t seed, int32_t* out_tokens, float* out_q, ssd_row_stats* out_stats,
+                              int32_t* out_topf_idx, float* out_topf_val, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* Target side: lossless acceptance test, accepted prefix and bonus token
+ * ([SSD-A]: the target accepts a prefix of the drafted tokens and samples one
+ * extra bonus token after them, and the output follows the target's
+ * distribution; [SSD-B] part 2: a rejected position's bonus comes from the
+ * residual p - q).
+ * For j = 0..K-1 in order: rho_j = p_j(x_j) / sigma_j(x_j) with p = softmax of
+ * the target row at temperature T and sigma_j rebuilt from the draft row
+ * (draft_stats, the first F entries of draft_topf_idx, C); u_j = Philox
+ * acceptance draw; accept iff u_j < rho_j; k* = number of leading accepts.
+ * Bonus: k* < K -> sample the normalised residual max(0, p_k* - sigma_k*)
+ * (p_k* if it has no mass); k* = K -> sample p_K.  Greedy sequences: accept
+ * iff x_j = argmax of the target row; bonus = argmax of target row k*.
+ *   target_logits, draft_logits  device [B, K+1, ld] rows of dtype dt
+ *   temperature  device float [B]; F, C as used for sampling; seed
+ *   draft_tokens device int32 [B, K]; ids outside [0, V) are rejected with
+ *                p = 0
+ *   draft_stats  device ssd_row_stats [B, K+1] from ssd_saguaro_sample
+ *   draft_topf_idx device int32 [B, K+1, ld_topf], ld_topf >= F (NULL if F=0)
+ * Outputs (device): out_accept_len int32 [B]; out_bonus int32 [B];
+ *   out_p float [B, K] = p_j(x_j) for every j; out_target_stats
+ *   ssd_row_stats [B, K+1] or NULL.
+ * workspace: ssd_workspace_bytes(SSD_OP_VERIFY, B, K, V). */
+ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K,
+                      int64_t V, int64_t ld, const float* temperature, int32_t F, float C, uint64_t seed,
+                      const int32_t* draft_tokens, const ssd_row_stats* draft_stats,
+                      const int32_t* draft_topf_idx, int32_t ld_topf, int32_t* out_accept_len,
+                      int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* Speculation-cache lookup keyed by (accepted length, bonus token) ([SSD-B]
+ * core-mechanism section: the draft builds a speculation cache while the
+ * target verifies and a single lookup follows; [SSD-A]: on a hit the prepared
+ * tokens go to the verifier at once).
+ *   keys      device int32 [B, Bgt]: depth-major, depth k at
+ *             [depth_off[k], depth_off[k+1])
+ *   depth_off device int32 [K+2], non-decreasing, depth_off[K+1] <= Bgt
+ *   payload   device int32 [B, Bgt, K]: the K pre-speculated tokens of a slot
+ *   accept_len, bonus  device int32 [B] (from ssd_verify)
+ * Outputs (device): out_hit int32 [B] (1/0); out_slot int32 [B] (lowest
+ * matching slot or -1); out_tokens int32 [B, K] (payload or -1).
+ * An accepted length outside [0, K] or offsets out of order give a miss. */
+ssd_status ssd_cache_lookup(const int32_t* keys, const int32_t* depth_off, const int32_t* payload, int32_t B,
+                            int32_t K, int32_t Bgt, const int32_t* accept_len, const int32_t* bonus,
+                            int32_t* out_hit, int32_t* out_slot, int32_t* out_tokens, void* stream);
+
+/* Build cache keys from per-row top-F lists: keys[b, depth_off[k] + i] =
+ * topf_idx[b, k, i] for i < F_k = depth_off[k+1] - depth_off[k] (F_k <=
+ * ld_topf, else the key is -1).  topf_idx device int32 [B, K+1, ld_topf];
+ * depth_off device int32 [K+2]; out_keys device int32 [B, Bgt]. */
+ssd_status ssd_cache_keys(const int32_t* topf_idx, int32_t ld_topf, const int32_t* depth_off, int32_t B,
+                          int32_t K, int32_t Bgt, int32_t* out_keys, void* stream);
+
+/* Fan-out F_k, k = 0..K, under budget Bgt ([SSD-B] part 1: the optimal
+ * per-depth fan-out is a truncated geometric series that shrinks with depth
+ * because the chance of accepting k tokens decays exponentially).  Reading:
+ * F_k proportional to ratio^k with sum exactly Bgt -- w_k = ratio^k by
+ * repeated multiplication from 1, S = w_0 + ... + w_K in order, ideal_k =
+ * Bgt * w_k / S (fp64), F_k = floor(ideal_k) and the remaining units go to
+ * the largest fractional parts, ties to the smaller k; each F_k is capped at
+ * V and the excess handed out in ascending k.  Pure host function.
+ *   out_F host int32 [K+1].  Errors: Bgt < 0, K < 0 or > SSD_MAX_K, ratio not
+ *   finite or <= 0, V < 1, Bgt > (K+1)*V. */
+ssd_status ssd_fanout(int32_t Bgt, int32_t K, double ratio, int64_t V, int32_t* out_F);
+
+/* Workspace bytes for `op`.  n = rows for SOFTMAX_T / TOPF (K ignored), n = B
+ * for SAMPLE / VERIFY.  Returns 0 for invalid sizes. */
+size_t ssd_workspace_bytes(ssd_op op, int64_t n, int32_t K, int64_t V);
+
+/* Static string naming a status. */
+const char* ssd_status_string(ssd_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

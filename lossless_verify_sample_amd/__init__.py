@@ -1,0 +1,272 @@
+"""Python binding of libssd, the gfx950 batched lossless verify-and-resample
+library (C ABI in include/ssd.h, which cites the method's sources).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+their pointers and torch's current HIP stream are passed to the C entry
+points, and every step of the path runs in the library's kernels.  PyTorch
+supplies device memory and streams.  The library is loaded from this
+package's directory; importing fails loudly if it has not been built
+(`python -m lossless_verify_sample_amd.build`).
+"""
+import ctypes
+import os
+
+import torch  # provides the process's HIP runtime, which libssd then shares
+
+__all__ = [
+    "SSDError", "softmax_t", "topf", "saguaro_sample", "verify", "cache_keys", "cache_lookup",
+    "fanout", "workspace_bytes", "stats_fields", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
+
+F32, BF16, F16 = 0, 1, 2
+OP_SOFTMAX_T, OP_TOPF, OP_SAMPLE, OP_VERIFY = 0, 1, 2, 3
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+_vp, _i32, _i64, _u64, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                           ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+
+
+class SSDError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m lossless_verify_sample_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "ssd_softmax_t": [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp],
+        "ssd_topf": [_vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp],
+        "ssd_saguaro_sample": [_vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _i32, _u64, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _sz, _vp],
+        "ssd_verify": [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _u64, _vp, _vp, _vp, _i32, _vp,
+                       _vp, _vp, _vp, _vp, _sz, _vp],
+        "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+        "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
+        "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ssd_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i32, _i64]
+    lib.ssd_workspace_bytes.restype = _sz
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+class _Lazy:
+    """The loaded library, on first use (a missing build raises ImportError)."""
+    lib = None
+
+    def __getattr__(self, name):
+        if _Lazy.lib is None:
+            _Lazy.lib = _load()
+        return getattr(_Lazy.lib, name)
+
+
+_lib = _Lazy()
+
+
+def library():
+    """The ctypes handle of libssd.so (loads it)."""
+    _lib.ssd_status_string
+    return _Lazy.lib
+
+
+def _check(st, name):
+    if st != 0:
+        raise SSDError(f"{name}: {_lib.ssd_status_string(st).decode()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, dtype, name, dev=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SSDError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise SSDError(f"{name} must be {dtype}, got {t.dtype}")
+    if dev is not None and t.device != dev:
+        raise SSDError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise SSDError(f"{name} must be contiguous")
+
+
+def _rows_ld(x, nd):
+    """Row stride of logits with the vocabulary contiguous and rows evenly spaced."""
+    if not x.is_cuda or x.dtype not in _DT:
+        raise SSDError("logits must be a device tensor of float32, bfloat16 or float16")
+    if x.dim() != nd or x.stride(-1) != 1:
+        raise SSDError(f"logits must be {nd}-D with a contiguous last dimension")
+    ld = x.stride(-2)
+    if nd == 3 and x.stride(0) != x.shape[1] * ld:
+        raise SSDError("logits rows must be evenly spaced")
+    return ld
+
+
+def workspace_bytes(op, n, K, V):
+    return int(_lib.ssd_workspace_bytes(op, n, K, V))
+
+
+_WS = {}
+
+
+def _workspace(op, n, K, V, dev):
+    """Zero-filled workspace, cached per (op, shape, device) and reused: each
+    call leaves its counters cleared.  Calls sharing one must not overlap."""
+    key = (op, n, K, V, dev)
+    w = _WS.get(key)
+    if w is None:
+        nb = workspace_bytes(op, n, K, V)
+        if nb == 0:
+            raise SSDError("invalid sizes for the workspace")
+        w = torch.zeros(nb + 256, dtype=torch.uint8, device=dev)
+        off = (-w.data_ptr()) % 256
+        w = w[off:off + nb]
+        _WS[key] = w
+    return w
+
+
+def _stats_tensor(n, dev):
+    return torch.empty((n, 2), dtype=torch.float64, device=dev)  # ssd_row_stats, 16 bytes
+
+
+def stats_fields(st):
+    """(lse float64, max float32, argmax int32) views of an ssd_row_stats tensor."""
+    flat = st.reshape(-1, 2)
+    return flat[:, 0], flat.view(torch.float32)[:, 2], flat.view(torch.int32)[:, 3]
+
+
+def softmax_t(logits, temperature, probs=False):
+    """Row statistics of softmax(z / T) for logits [R, V]; optional dense probs."""
+    ld = _rows_ld(logits, 2)
+    R, V = logits.shape
+    dev = logits.device
+    _need(temperature, torch.float32, "temperature", dev)
+    if temperature.numel() != R:
+        raise SSDError("temperature must have one entry per row")
+    st = _stats_tensor(R, dev)
+    pr = torch.empty((R, V), dtype=torch.float32, device=dev) if probs else None
+    ws = _workspace(OP_SOFTMAX_T, R, 0, V, dev)
+    _check(_lib.ssd_softmax_t(_p(logits), _DT[logits.dtype], R, V, ld, _p(temperature), _p(st), _p(pr),
+                              _p(ws), ws.numel(), _stream(dev)), "ssd_softmax_t")
+    return st, pr
+
+
+def topf(logits, F):
+    """Top-F raw logits per row of [R, V]: (idx int32 [R, F], val float32 [R, F])."""
+    ld = _rows_ld(logits, 2)
+    R, V = logits.shape
+    dev = logits.device
+    idx = torch.empty((R, F), dtype=torch.int32, device=dev)
+    val = torch.empty((R, F), dtype=torch.float32, device=dev)
+    ws = _workspace(OP_TOPF, R, 0, V, dev)
+    _check(_lib.ssd_topf(_p(logits), _DT[logits.dtype], R, V, ld, F, _p(idx), _p(val), _p(ws), ws.numel(),
+                         _stream(dev)), "ssd_topf")
+    return idx, val
+
+
+def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None):
+    """Draft sampling with sigma_{F,C} over draft logits [B, K+1, V].
+
+    Returns dict(tokens [B,K] int32, q [B,K] f32, stats [B*(K+1), 2] (see
+    stats_fields), topf_idx [B,K+1,F_out] int32, topf_val [B,K+1,F_out] f32).
+    `out` may pass a dict of preallocated outputs with those keys."""
+    ld = _rows_ld(draft, 3)
+    B, K1, V = draft.shape
+    K = K1 - 1
+    dev = draft.device
+    F_out = F if F_out is None else F_out
+    _need(temperature, torch.float32, "temperature", dev)
+    if temperature.numel() != B:
+        raise SSDError("temperature must have one entry per sequence")
+    if out is None:
+        out = dict(tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
+                   q=torch.empty((B, K), dtype=torch.float32, device=dev),
+                   stats=_stats_tensor(B * K1, dev),
+                   topf_idx=torch.empty((B, K1, F_out), dtype=torch.int32, device=dev),
+                   topf_val=torch.empty((B, K1, F_out), dtype=torch.float32, device=dev))
+    ws = _workspace(OP_SAMPLE, B, K, V, dev)
+    _check(_lib.ssd_saguaro_sample(_p(draft), _DT[draft.dtype], B, K, V, ld, _p(temperature), F, float(C), F_out,
+                                   int(seed) & (2 ** 64 - 1), _p(out["tokens"]), _p(out["q"]), _p(out["stats"]),
+                                   _p(out["topf_idx"]), _p(out["topf_val"]), _p(ws), ws.numel(), _stream(dev)),
+           "ssd_saguaro_sample")
+    return out
+
+
+def verify(target, draft, temperature, F, C, seed, tokens, draft_stats, draft_topf_idx, want_stats=False,
+           out=None):
+    """Acceptance test, accepted length and bonus for target/draft [B, K+1, V].
+
+    Returns dict(accept_len [B] int32, bonus [B] int32, p [B,K] f32, stats
+    [B*(K+1), 2] or None)."""
+    ld = _rows_ld(target, 3)
+    if draft.shape != target.shape or draft.dtype != target.dtype or _rows_ld(draft, 3) != ld:
+        raise SSDError("target and draft logits must share shape, dtype and row stride")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _need(temperature, torch.float32, "temperature", dev)
+    _need(tokens, torch.int32, "tokens", dev)
+    _need(draft_stats, torch.float64, "draft_stats", dev)
+    ldf = 0
+    if F > 0:
+        _need(draft_topf_idx, torch.int32, "draft_topf_idx", dev)
+        ldf = draft_topf_idx.shape[-1]
+    if out is None:
+        out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   bonus=torch.empty(B, dtype=torch.int32, device=dev),
+                   p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                   stats=_stats_tensor(B * K1, dev) if want_stats else None)
+    ws = _workspace(OP_VERIFY, B, K, V, dev)
+    _check(_lib.ssd_verify(_p(target), _p(draft), _DT[target.dtype], B, K, V, ld, _p(temperature), F, float(C),
+                           int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_stats),
+                           _p(draft_topf_idx) if F > 0 else None, ldf, _p(out["accept_len"]), _p(out["bonus"]),
+                           _p(out["p"]), _p(out.get("stats")), _p(ws), ws.numel(), _stream(dev)), "ssd_verify")
+    return out
+
+
+def cache_keys(topf_idx, depth_off, Bgt):
+    """keys [B, Bgt] int32 from per-row top-F lists [B, K+1, ldf] and depth offsets [K+2]."""
+    _need(topf_idx, torch.int32, "topf_idx")
+    dev = topf_idx.device
+    _need(depth_off, torch.int32, "depth_off", dev)
+    B, K1, ldf = topf_idx.shape
+    keys = torch.empty((B, Bgt), dtype=torch.int32, device=dev)
+    _check(_lib.ssd_cache_keys(_p(topf_idx), ldf, _p(depth_off), B, K1 - 1, Bgt, _p(keys), _stream(dev)),
+           "ssd_cache_keys")
+    return keys
+
+
+def cache_lookup(keys, depth_off, payload, accept_len, bonus):
+    """(hit [B], slot [B], tokens [B, K]) int32 for the realised (accepted length, bonus)."""
+    _need(keys, torch.int32, "keys")
+    dev = keys.device
+    for t, n in ((depth_off, "depth_off"), (payload, "payload"), (accept_len, "accept_len"), (bonus, "bonus")):
+        _need(t, torch.int32, n, dev)
+    B, Bgt = keys.shape
+    K = payload.shape[2]
+    if payload.shape[:2] != (B, Bgt) or depth_off.numel() != K + 2:
+        raise SSDError("payload must be [B, Bgt, K] and depth_off [K+2]")
+    hit = torch.empty(B, dtype=torch.int32, device=dev)
+    slot = torch.empty(B, dtype=torch.int32, device=dev)
+    toks = torch.empty((B, K), dtype=torch.int32, device=dev)
+    _check(_lib.ssd_cache_lookup(_p(keys), _p(depth_off), _p(payload), B, K, Bgt, _p(accept_len), _p(bonus),
+                                 _p(hit), _p(slot), _p(toks), _stream(dev)), "ssd_cache_lookup")
+    return hit, slot, toks
+
+
+def fanout(Bgt, K, ratio, V):
+    """Per-depth fan-out F_0..F_K under budget Bgt (host computation in libssd)."""
+    arr = (ctypes.c_int32 * (K + 1))()
+    _check(_lib.ssd_fanout(Bgt, K, float(ratio), V, arr), "ssd_fanout")
+    return list(arr)

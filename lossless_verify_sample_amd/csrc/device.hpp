@@ -1,0 +1,324 @@
+// Device building blocks for gfx950: dtype decode, 16-byte streaming loads,
+// wave64 reductions on DPP, workgroup reductions through LDS, Philox4x32-10,
+// uniforms and Gumbel draws.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd.h"
+
+namespace ssd {
+
+constexpr int BLK = SSD_BLOCK;   // vocabulary block (two-level sampler, partials)
+constexpr int WG = 256;          // threads per workgroup
+constexpr int NWAVE = WG / 64;   // wave64s per workgroup
+constexpr int MAX_NB = SSD_MAX_V / SSD_BLOCK;
+constexpr int CAND_CAP = 256;    // top-F candidate list held in LDS
+constexpr int MAX_F = SSD_MAX_F;
+constexpr int MAX_K1 = SSD_MAX_K + 1;
+constexpr int STAGE = 1024;      // partials staged in LDS by the verify epilogue
+
+constexpr double LOG2E = 1.4426950408889634073599246810019;
+constexpr double LN2 = 0.69314718055994530941723212145818;
+
+// ---------------------------------------------------------------------------
+// dtype traits: bytes per element, elements per 16-byte chunk, decode
+// ---------------------------------------------------------------------------
+template <int DT> struct Dt;
+template <> struct Dt<SSD_F32> { static constexpr int SZ = 4; static constexpr int VW = 4; };
+template <> struct Dt<SSD_BF16> { static constexpr int SZ = 2; static constexpr int VW = 8; };
+template <> struct Dt<SSD_F16> { static constexpr int SZ = 2; static constexpr int VW = 8; };
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <int DT>
+__device__ __forceinline__ void decode16(const uint4 w, float* o) {
+  if constexpr (DT == SSD_F32) {
+    o[0] = __uint_as_float(w.x); o[1] = __uint_as_float(w.y);
+    o[2] = __uint_as_float(w.z); o[3] = __uint_as_float(w.w);
+  } else if constexpr (DT == SSD_BF16) {
+    o[0] = bf16lo(w.x); o[1] = bf16hi(w.x); o[2] = bf16lo(w.y); o[3] = bf16hi(w.y);
+    o[4] = bf16lo(w.z); o[5] = bf16hi(w.z); o[6] = bf16lo(w.w); o[7] = bf16hi(w.w);
+  } else {
+    o[0] = f16lo(w.x); o[1] = f16hi(w.x); o[2] = f16lo(w.y); o[3] = f16hi(w.y);
+    o[4] = f16lo(w.z); o[5] = f16hi(w.z); o[6] = f16lo(w.w); o[7] = f16hi(w.w);
+  }
+}
+
+// One element (any alignment).
+template <int DT>
+__device__ __forceinline__ float load_elem(const unsigned char* row, int64_t i) {
+  if constexpr (DT == SSD_F32) {
+    return reinterpret_cast<const float*>(row)[i];
+  } else {
+    uint32_t h = reinterpret_cast<const uint16_t*>(row)[i];
+    return DT == SSD_BF16 ? __uint_as_float(h << 16)
+                          : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  }
+}
+
+// VW consecutive elements from e0: one 16-byte load on the aligned path (the
+// host only takes it when base, row stride and V are all 16-byte multiples,
+// so a chunk is either wholly inside the row or wholly past its end), else
+// guarded element loads.  Elements at or past V read as -inf.
+template <int DT, bool AL>
+__device__ __forceinline__ void load_chunk(const unsigned char* row, int64_t V, int64_t e0, float* o) {
+  constexpr int VW = Dt<DT>::VW;
+  if constexpr (AL) {
+    if (e0 < V) {
+      const uint4 w = *reinterpret_cast<const uint4*>(row + e0 * Dt<DT>::SZ);
+      decode16<DT>(w, o);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) o[e] = -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VW; ++e) o[e] = (e0 + e < V) ? load_elem<DT>(row, e0 + e) : -INFINITY;
+  }
+}
+
+// The 32 elements a lane owns in block beta: chunks lane + 64*i, i < 32/VW.
+// Element k = i*VW + e sits at beta*BLK + (i*64 + lane)*VW + e.
+template <int DT, bool AL>
+__device__ __forceinline__ void load_block(const unsigned char* row, int64_t V, int64_t beta, int lane,
+                                           float (&v)[32]) {
+  constexpr int VW = Dt<DT>::VW;
+#pragma unroll
+  for (int i = 0; i < 32 / VW; ++i)
+    load_chunk<DT, AL>(row, V, beta * BLK + (int64_t)(i * 64 + lane) * VW, &v[i * VW]);
+}
+
+// Element indices fit in int32 (V <= 2^20).
+template <int DT>
+__device__ __forceinline__ int block_elem_index(int beta, int lane, int k) {
+  constexpr int VW = Dt<DT>::VW;
+  return beta * BLK + ((k / VW) * 64 + lane) * VW + (k % VW);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions.  Inside each row of 16 lanes a butterfly of DPP moves
+// (quad xor 1, quad xor 2, half-row mirror, row mirror) leaves the row's
+// result in every lane; the four rows are then combined from lanes 0, 16,
+// 32, 48 in a fixed order.  The whole wave must be active.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const int lo = dpp_i<CTRL>((int)(uint32_t)u), hi = dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t u) {
+  const int lo = dpp_i<CTRL>((int)(uint32_t)u), hi = dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+constexpr int DPP_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_HMIR = 0x141;  // row_half_mirror
+constexpr int DPP_MIR = 0x140;   // row_mirror
+
+__device__ __forceinline__ float rl_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double rl_d(double x, int l) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ uint64_t rl_u64(uint64_t u, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<DPP_XOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_XOR2>(x));
+  x = fmaxf(x, dpp_f<DPP_HMIR>(x));
+  x = fmaxf(x, dpp_f<DPP_MIR>(x));
+  return fmaxf(fmaxf(rl_f(x, 0), rl_f(x, 16)), fmaxf(rl_f(x, 32), rl_f(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = x + dpp_f<DPP_XOR1>(x);
+  x = x + dpp_f<DPP_XOR2>(x);
+  x = x + dpp_f<DPP_HMIR>(x);
+  x = x + dpp_f<DPP_MIR>(x);
+  return (rl_f(x, 0) + rl_f(x, 16)) + (rl_f(x, 32) + rl_f(x, 48));
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x = x + dpp_d<DPP_XOR1>(x);
+  x = x + dpp_d<DPP_XOR2>(x);
+  x = x + dpp_d<DPP_HMIR>(x);
+  x = x + dpp_d<DPP_MIR>(x);
+  return (rl_d(x, 0) + rl_d(x, 16)) + (rl_d(x, 32) + rl_d(x, 48));
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = umax64(x, dpp_u64<DPP_XOR1>(x));
+  x = umax64(x, dpp_u64<DPP_XOR2>(x));
+  x = umax64(x, dpp_u64<DPP_HMIR>(x));
+  x = umax64(x, dpp_u64<DPP_MIR>(x));
+  return umax64(umax64(rl_u64(x, 0), rl_u64(x, 16)), umax64(rl_u64(x, 32), rl_u64(x, 48)));
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+  x = min(x, dpp_i<DPP_XOR1>(x));
+  x = min(x, dpp_i<DPP_XOR2>(x));
+  x = min(x, dpp_i<DPP_HMIR>(x));
+  x = min(x, dpp_i<DPP_MIR>(x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// (score desc, index asc) arg-max on doubles.
+struct Arg {
+  double s;
+  int64_t i;
+};
+__device__ __forceinline__ Arg better(Arg a, Arg b) {
+  return (b.s > a.s || (b.s == a.s && b.i < a.i)) ? b : a;
+}
+template <int CTRL>
+__device__ __forceinline__ Arg dpp_arg(Arg a) {
+  return Arg{dpp_d<CTRL>(a.s), (int64_t)dpp_u64<CTRL>((uint64_t)a.i)};
+}
+__device__ __forceinline__ Arg wave_argmax(Arg a) {
+  a = better(a, dpp_arg<DPP_XOR1>(a));
+  a = better(a, dpp_arg<DPP_XOR2>(a));
+  a = better(a, dpp_arg<DPP_HMIR>(a));
+  a = better(a, dpp_arg<DPP_MIR>(a));
+  Arg r0{rl_d(a.s, 0), (int64_t)rl_u64((uint64_t)a.i, 0)};
+  Arg r1{rl_d(a.s, 16), (int64_t)rl_u64((uint64_t)a.i, 16)};
+  Arg r2{rl_d(a.s, 32), (int64_t)rl_u64((uint64_t)a.i, 32)};
+  Arg r3{rl_d(a.s, 48), (int64_t)rl_u64((uint64_t)a.i, 48)};
+  return better(better(r0, r1), better(r2, r3));
+}
+
+// ---------------------------------------------------------------------------
+// workgroup reductions (every thread of the workgroup must call; all get the
+// result).  `red` is LDS scratch of at least NWAVE entries of 16 bytes.
+// ---------------------------------------------------------------------------
+struct Red {
+  double d[NWAVE];
+  int64_t i[NWAVE];
+};
+
+__device__ __forceinline__ float wg_max(float x, Red& r) {
+  x = wave_max(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.d[w] = x;
+  __syncthreads();
+  float m = (float)r.d[0];
+  for (int k = 1; k < NWAVE; ++k) m = fmaxf(m, (float)r.d[k]);
+  return m;
+}
+__device__ __forceinline__ double wg_sum_d(double x, Red& r) {
+  x = wave_sum_d(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.d[w] = x;
+  __syncthreads();
+  return (r.d[0] + r.d[1]) + (r.d[2] + r.d[3]);
+}
+__device__ __forceinline__ Arg wg_argmax(Arg a, Red& r) {
+  a = wave_argmax(a);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { r.d[w] = a.s; r.i[w] = a.i; }
+  __syncthreads();
+  Arg b{r.d[0], r.i[0]};
+  for (int k = 1; k < NWAVE; ++k) b = better(b, Arg{r.d[k], r.i[k]});
+  return b;
+}
+__device__ __forceinline__ uint64_t wg_max_u64(uint64_t x, Red& r) {
+  x = wave_max_u64(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.i[w] = (int64_t)x;
+  __syncthreads();
+  uint64_t m = (uint64_t)r.i[0];
+  for (int k = 1; k < NWAVE; ++k) m = umax64(m, (uint64_t)r.i[k]);
+  return m;
+}
+
+// Order-preserving key of (value desc, index asc): larger key = better.
+__device__ __forceinline__ uint64_t vi_key(float v, int64_t idx) {
+  uint32_t b = __float_as_uint(v + 0.0f);  // -0 -> +0
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ float key_val(uint64_t k) {
+  uint32_t b = (uint32_t)(k >> 32);
+  b = (b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b;
+  return __uint_as_float(b);
+}
+__device__ __forceinline__ int64_t key_idx(uint64_t k) {
+  return (int64_t)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64-bit
+// multiplies with a Weyl key schedule.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1,
+                   (uint32_t)p0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+enum Stream : uint32_t {
+  ST_DRAFT_TOKEN = 0,
+  ST_DRAFT_BLOCK = 1,
+  ST_ACCEPT = 2,
+  ST_BONUS_TOKEN = 3,
+  ST_BONUS_BLOCK = 4,
+  ST_FALLBACK = 5
+};
+
+// Four draws idx = 4c .. 4c+3 of stream `st` at (b, j).
+__device__ __forceinline__ uint4 draws4(uint64_t seed, uint32_t c, uint32_t b, uint32_t j, uint32_t st) {
+  return philox(make_uint4(c, b, j, st), (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+__device__ __forceinline__ uint32_t draw1(uint64_t seed, uint32_t idx, uint32_t b, uint32_t j, uint32_t st) {
+  const uint4 w = draws4(seed, idx >> 2, b, j, st);
+  const uint32_t s = idx & 3u;
+  return s == 0 ? w.x : s == 1 ? w.y : s == 2 ? w.z : w.w;
+}
+// u = ((w >> 9) + 0.5) * 2^-23: an odd multiple of 2^-24, exact in binary32.
+__device__ __forceinline__ float uniform_of(uint32_t w) {
+  return (float)(((w >> 9) << 1) | 1u) * 5.9604644775390625e-8f;  // 2^-24
+}
+// g = -ln(-ln u); -ln u from log1p(u - 1) above 1/2 (u - 1 is exact there).
+__device__ __forceinline__ float gumbel_of(uint32_t w) {
+  const float u = uniform_of(w);
+  const float t = u > 0.5f ? -log1pf(u - 1.0f) : -logf(u);
+  return -logf(t);
+}
+
+}  // namespace ssd

@@ -1,0 +1,311 @@
+// C ABI of the verify-and-resample library (declarations and citations in
+// include/ssd.h): host-side argument checks, workspace layout and launches.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kernels.hpp"
+
+using namespace ssd;
+
+namespace {
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+int dt_size(int dt) { return dt == SSD_F32 ? 4 : 2; }
+bool dt_ok(int dt) { return dt == SSD_F32 || dt == SSD_BF16 || dt == SSD_F16; }
+int64_t nblocks(int64_t V) { return (V + BLK - 1) / BLK; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Layout {
+  size_t part, cnt, state, rpart, rcnt, total;
+};
+
+bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
+  if (n < 1 || V < 1 || V > SSD_MAX_V) return false;
+  if ((op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY) && (K < 0 || K > SSD_MAX_K)) return false;
+  if (op != SSD_OP_SOFTMAX_T && op != SSD_OP_TOPF && op != SSD_OP_SAMPLE && op != SSD_OP_VERIFY) return false;
+  const int64_t NB = nblocks(V);
+  const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY) ? n * (K + 1) : n;
+  const int64_t groups = (op == SSD_OP_VERIFY) ? n : rows;
+  L->part = 0;
+  L->cnt = al256((size_t)(rows * NB) * sizeof(float2));
+  L->state = L->cnt + al256((size_t)groups * sizeof(unsigned));
+  if (op == SSD_OP_VERIFY) {
+    L->rpart = L->state + al256((size_t)n * sizeof(SeqState));
+    L->rcnt = L->rpart + al256((size_t)(n * NB) * sizeof(float));
+    L->total = L->rcnt + al256((size_t)n * sizeof(unsigned));
+  } else {
+    L->rpart = L->rcnt = 0;
+    L->total = L->state;
+  }
+  return true;
+}
+
+bool aligned16(const void* ptr, int64_t ld, int64_t V, int dt) {
+  const int sz = dt_size(dt);
+  return ((uintptr_t)ptr % 16 == 0) && ((ld * sz) % 16 == 0) && ((V * sz) % 16 == 0);
+}
+
+template <template <int, bool> class L, class... A>
+hipError_t dispatch(int dt, bool al, A... a) {
+  if (dt == SSD_F32) return al ? L<SSD_F32, true>::go(a...) : L<SSD_F32, false>::go(a...);
+  if (dt == SSD_BF16) return al ? L<SSD_BF16, true>::go(a...) : L<SSD_BF16, false>::go(a...);
+  return al ? L<SSD_F16, true>::go(a...) : L<SSD_F16, false>::go(a...);
+}
+
+#define SSD_LAUNCHER(NAME, KERNEL)                                                   \
+  template <int DT, bool AL>                                                         \
+  struct NAME {                                                                      \
+    static hipError_t go(int64_t grid, const Params& p, hipStream_t st) {            \
+      KERNEL<<<dim3((unsigned)grid), dim3(WG), 0, st>>>(p);                          \
+      return hipGetLastError();                                                      \
+    }                                                                                \
+  };
+
+SSD_LAUNCHER(LSoftmax, (k_stream<DT, AL, M_SOFTMAX>))
+SSD_LAUNCHER(LTopf, (k_stream<DT, AL, M_TOPF>))
+SSD_LAUNCHER(LSample, (k_stream<DT, AL, M_SAMPLE>))
+SSD_LAUNCHER(LVerify, (k_stream<DT, AL, M_VERIFY>))
+SSD_LAUNCHER(LResidual, (k_residual<DT, AL>))
+SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
+
+ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
+  return ws != nullptr && ((uintptr_t)ws % 256 == 0) && bytes >= L.total;
+}
+
+const int64_t kMaxGrid = 0x7fffffff;
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(ssd_status s) {
+  switch (s) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_INVALID_ARG: return "SSD_ERR_INVALID_ARG";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+  }
+  return "SSD_ERR_UNKNOWN";
+}
+
+size_t ssd_workspace_bytes(ssd_op op, int64_t n, int32_t K, int64_t V) {
+  Layout L;
+  return layout(op, n, K, V, &L) ? L.total : 0;
+}
+
+ssd_status ssd_softmax_t(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, int64_t ld,
+                         const float* temperature, ssd_row_stats* out_stats, float* out_probs,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  if (!logits || !temperature || !out_stats || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
+  if (rows < 1 || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
+  Layout L;
+  if (!layout(SSD_OP_SOFTMAX_T, rows, 0, V, &L)) return SSD_ERR_INVALID_ARG;
+  if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
+  if (rows * nch > kMaxGrid || rows * cdiv(NB, NWAVE) > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  Params p{};
+  p.x = (const unsigned char*)logits;
+  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
+  p.temp = temperature;
+  char* ws = (char*)workspace;
+  p.part = (float2*)(ws + L.part);
+  p.cnt = (unsigned*)(ws + L.cnt);
+  p.stats = out_stats;
+  p.probs = out_probs;
+  const bool al = aligned16(logits, ld, V, dt);
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipError_t e = dispatch<LSoftmax>(dt, al, rows * nch, p, st);
+  if (e == hipSuccess && out_probs) {
+    p.nchunk = (int)cdiv(NB, NWAVE);
+    e = dispatch<LProbs>(dt, al, rows * p.nchunk, p, st);
+  }
+  return hip_status(e);
+}
+
+ssd_status ssd_topf(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, int64_t ld, int32_t F,
+                    int32_t* out_idx, float* out_val, void* workspace, size_t ws_bytes, void* stream) {
+  if (!logits || !out_idx || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
+  if (rows < 1 || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
+  if (F < 1 || F > SSD_MAX_F || F > V) return SSD_ERR_INVALID_ARG;
+  Layout L;
+  if (!layout(SSD_OP_TOPF, rows, 0, V, &L)) return SSD_ERR_INVALID_ARG;
+  if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
+  if (rows * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  Params p{};
+  p.x = (const unsigned char*)logits;
+  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
+  p.F = F; p.F_sel = F;
+  char* ws = (char*)workspace;
+  p.part = (float2*)(ws + L.part);
+  p.cnt = (unsigned*)(ws + L.cnt);
+  p.out_idx = out_idx;
+  p.out_val = out_val;
+  (void)hipGetLastError();
+  return hip_status(dispatch<LTopf>(dt, aligned16(logits, ld, V, dt), rows * nch, p, (hipStream_t)stream));
+}
+
+ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K, int64_t V,
+                              int64_t ld, const float* temperature, int32_t F, float C, int32_t F_out,
+                              uint64_t seed, int32_t* out_tokens, float* out_q, ssd_row_stats* out_stats,
+                              int32_t* out_topf_idx, float* out_topf_val, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  if (!draft_logits || !temperature || !out_stats || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
+  if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
+  if (K > 0 && (!out_tokens || !out_q)) return SSD_ERR_INVALID_ARG;
+  if (F < 0 || F > SSD_MAX_F || F > V || F_out < F || F_out > SSD_MAX_F || F_out > V) return SSD_ERR_INVALID_ARG;
+  if (F_out > 0 && !out_topf_idx && !out_topf_val) return SSD_ERR_INVALID_ARG;
+  if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
+  Layout L;
+  if (!layout(SSD_OP_SAMPLE, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
+  if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * (K + 1);
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
+  if (rows * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  Params p{};
+  p.x = (const unsigned char*)draft_logits;
+  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
+  p.K = K; p.B = B;
+  p.temp = temperature;
+  p.F = F; p.F_out = F_out; p.F_sel = F_out > 1 ? F_out : 1;
+  p.C = C; p.seed = seed;
+  char* ws = (char*)workspace;
+  p.part = (float2*)(ws + L.part);
+  p.cnt = (unsigned*)(ws + L.cnt);
+  p.stats = out_stats;
+  p.out_idx = F_out > 0 ? out_topf_idx : nullptr;
+  p.out_val = F_out > 0 ? out_topf_val : nullptr;
+  p.tokens = out_tokens;
+  p.q = out_q;
+  (void)hipGetLastError();
+  return hip_status(dispatch<LSample>(dt, aligned16(draft_logits, ld, V, dt), rows * nch, p, (hipStream_t)stream));
+}
+
+ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K,
+                      int64_t V, int64_t ld, const float* temperature, int32_t F, float C, uint64_t seed,
+                      const int32_t* draft_tokens, const ssd_row_stats* draft_stats,
+                      const int32_t* draft_topf_idx, int32_t ld_topf, int32_t* out_accept_len,
+                      int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  if (!target_logits || !draft_logits || !temperature || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
+  if (!draft_stats || !out_accept_len || !out_bonus) return SSD_ERR_INVALID_ARG;
+  if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
+  if (K > 0 && (!draft_tokens || !out_p)) return SSD_ERR_INVALID_ARG;
+  if (F < 0 || F > SSD_MAX_F || F > V) return SSD_ERR_INVALID_ARG;
+  if (F > 0 && (!draft_topf_idx || ld_topf < F)) return SSD_ERR_INVALID_ARG;
+  if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
+  Layout L;
+  if (!layout(SSD_OP_VERIFY, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
+  if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * (K + 1);
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH), nchr = cdiv(NB, CH_R);
+  if (rows * nch > kMaxGrid || (int64_t)B * nchr > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  Params p{};
+  p.x = (const unsigned char*)target_logits;
+  p.xd = (const unsigned char*)draft_logits;
+  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
+  p.K = K; p.B = B;
+  p.temp = temperature;
+  p.F = F; p.C = C; p.seed = seed;
+  char* ws = (char*)workspace;
+  p.part = (float2*)(ws + L.part);
+  p.cnt = (unsigned*)(ws + L.cnt);
+  p.state = (SeqState*)(ws + L.state);
+  p.rpart = (float*)(ws + L.rpart);
+  p.rcnt = (unsigned*)(ws + L.rcnt);
+  p.stats = out_target_stats;
+  p.dtok = draft_tokens;
+  p.dstats = draft_stats;
+  p.dtopf = F > 0 ? draft_topf_idx : nullptr;
+  p.ld_dtopf = ld_topf;
+  p.acc_len = out_accept_len;
+  p.bonus = out_bonus;
+  p.p_out = out_p;
+  const bool al = aligned16(target_logits, ld, V, dt) && aligned16(draft_logits, ld, V, dt);
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipError_t e = dispatch<LVerify>(dt, al, rows * nch, p, st);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  p.nchunk = (int)nchr;
+  return hip_status(dispatch<LResidual>(dt, al, (int64_t)B * nchr, p, st));
+}
+
+ssd_status ssd_cache_lookup(const int32_t* keys, const int32_t* depth_off, const int32_t* payload, int32_t B,
+                            int32_t K, int32_t Bgt, const int32_t* accept_len, const int32_t* bonus,
+                            int32_t* out_hit, int32_t* out_slot, int32_t* out_tokens, void* stream) {
+  if (B < 1 || K < 0 || K > SSD_MAX_K || Bgt < 0) return SSD_ERR_INVALID_ARG;
+  if (!depth_off || !accept_len || !bonus || !out_hit || !out_slot) return SSD_ERR_INVALID_ARG;
+  if (Bgt > 0 && !keys) return SSD_ERR_INVALID_ARG;
+  if (K > 0 && Bgt > 0 && !payload) return SSD_ERR_INVALID_ARG;
+  if (K > 0 && !out_tokens) return SSD_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  k_lookup<<<dim3((unsigned)cdiv(B, NWAVE)), dim3(WG), 0, (hipStream_t)stream>>>(
+      keys, depth_off, payload, B, K, Bgt, accept_len, bonus, out_hit, out_slot, out_tokens);
+  return hip_status(hipGetLastError());
+}
+
+ssd_status ssd_cache_keys(const int32_t* topf_idx, int32_t ld_topf, const int32_t* depth_off, int32_t B,
+                          int32_t K, int32_t Bgt, int32_t* out_keys, void* stream) {
+  if (B < 1 || K < 0 || K > SSD_MAX_K || Bgt < 0 || ld_topf < 0) return SSD_ERR_INVALID_ARG;
+  if (!depth_off || (Bgt > 0 && (!out_keys || (ld_topf > 0 && !topf_idx)))) return SSD_ERR_INVALID_ARG;
+  if (Bgt == 0) return SSD_OK;
+  const int64_t n = (int64_t)B * Bgt;
+  if (cdiv(n, WG) > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  k_cache_keys<<<dim3((unsigned)cdiv(n, WG)), dim3(WG), 0, (hipStream_t)stream>>>(topf_idx, ld_topf, depth_off,
+                                                                                  B, K, Bgt, out_keys);
+  return hip_status(hipGetLastError());
+}
+
+ssd_status ssd_fanout(int32_t Bgt, int32_t K, double ratio, int64_t V, int32_t* out_F) {
+  if (!out_F || Bgt < 0 || K < 0 || K > SSD_MAX_K || V < 1) return SSD_ERR_INVALID_ARG;
+  if (!isfinite(ratio) || !(ratio > 0.0)) return SSD_ERR_INVALID_ARG;
+  if ((int64_t)Bgt > (int64_t)(K + 1) * V) return SSD_ERR_INVALID_ARG;
+  double w[SSD_MAX_K + 1], ideal[SSD_MAX_K + 1], frac[SSD_MAX_K + 1];
+  int64_t F[SSD_MAX_K + 1];
+  double x = 1.0;
+  for (int k = 0; k <= K; ++k) {
+    w[k] = x;
+    x = x * ratio;
+  }
+  double S = 0.0;
+  for (int k = 0; k <= K; ++k) S = S + w[k];
+  int64_t used = 0;
+  for (int k = 0; k <= K; ++k) {
+    ideal[k] = (double)Bgt * w[k] / S;
+    const double fl = floor(ideal[k]);
+    F[k] = (int64_t)fl;
+    frac[k] = ideal[k] - fl;
+    used += F[k];
+  }
+  int64_t rem = (int64_t)Bgt - used;
+  bool taken[SSD_MAX_K + 1] = {};
+  while (rem > 0) {  // largest fractional part first, ties to the smaller k
+    int best = -1;
+    for (int k = 0; k <= K; ++k)
+      if (!taken[k] && (best < 0 || frac[k] > frac[best])) best = k;
+    taken[best] = true;
+    F[best] += 1;
+    --rem;
+  }
+  int64_t excess = 0;
+  for (int k = 0; k <= K; ++k)
+    if (F[k] > V) {
+      excess += F[k] - V;
+      F[k] = V;
+    }
+  for (int k = 0; k <= K && excess > 0; ++k) {
+    const int64_t give = excess < V - F[k] ? excess : V - F[k];
+    F[k] += give;
+    excess -= give;
+  }
+  for (int k = 0; k <= K; ++k) out_F[k] = (int32_t)F[k];
+  return SSD_OK;
+}
+
+}  // extern "C"

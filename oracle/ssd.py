@@ -93,7 +93,14 @@ def topf(z, F):
     """Indices and values of the F largest raw logits, ordered by value
     descending then index ascending (ranking on raw z, not z/T)."""
     z = np.asarray(z, dtype=np.float64)
-    order = np.lexsort((np.arange(z.shape[0]), -z))
+    V = z.shape[0]
+    if F <= 0:
+        return np.zeros(0, np.int64), np.zeros(0)
+    # every top-F element is >= the F-th largest value (library selection),
+    # so only those are sorted
+    thr = np.partition(z, V - F)[V - F]
+    cand = np.nonzero(z >= thr)[0]
+    order = cand[np.lexsort((cand, -z[cand]))]
     idx = order[:F]
     return idx.astype(np.int64), z[idx]
 
@@ -161,8 +168,9 @@ def gsample(w, seed, b, j, tok_stream, blk_stream, blk=BLK):
 # --------------------------------------------------------------------------
 # draft side: sigma_{F,C} sampling of K tokens plus row statistics and top-F
 # --------------------------------------------------------------------------
-def draft_sample(zd, T, F, C, seed, F_out=None, blk=BLK):
-    """zd: [B, K+1, V] fp64 draft logits; T: [B] temperatures.
+def draft_sample(zd, T, F, C, seed, F_out=None, blk=BLK, b0=0):
+    """zd: [B, K+1, V] fp64 draft logits; T: [B] temperatures.  b0 is the
+    batch index of the first sequence (its Philox counters use b0 + b).
 
     For positions j < K the token x_j ~ sigma_j is drawn with the two-level
     sampler (streams DRAFT_TOKEN / DRAFT_BLOCK); greedy rows take the argmax.
@@ -195,7 +203,7 @@ def draft_sample(zd, T, F, C, seed, F_out=None, blk=BLK):
             if is_greedy(T[b]):
                 x, mg = sg["argmax"], math.inf
             else:
-                x, mg = gsample(sg["sigma"], seed, b, j, ph.DRAFT_TOKEN, ph.DRAFT_BLOCK, blk)
+                x, mg = gsample(sg["sigma"], seed, b0 + b, j, ph.DRAFT_TOKEN, ph.DRAFT_BLOCK, blk)
             out["tokens"][b, j] = x
             out["q"][b, j] = sg["sigma"][x]
             out["margin"][b, j] = mg
@@ -222,8 +230,9 @@ def residual(p, s):
     return r / t if t > 0 else p.copy()
 
 
-def verify(zt, zd, T, F, C, seed, tokens, blk=BLK):
-    """zt, zd: [B, K+1, V] fp64; T: [B]; tokens: [B, K] drafted tokens.
+def verify(zt, zd, T, F, C, seed, tokens, blk=BLK, b0=0):
+    """zt, zd: [B, K+1, V] fp64; T: [B]; tokens: [B, K] drafted tokens;
+    b0: batch index of the first sequence (Philox counters use b0 + b).
 
     For j = 0..K-1 in order: rho_j = p_j(x_j) / sigma_j(x_j);
     u_j = U(seed, b, j, ACCEPT, idx 0); accept iff u_j < rho_j; stop at the
@@ -270,7 +279,7 @@ def verify(zt, zd, T, F, C, seed, tokens, blk=BLK):
                     rho = pj / s[x]
                 else:
                     rho = math.inf if pj > 0 else 0.0
-                u = float(ph.uniforms(seed, b, j, ph.ACCEPT, np.array([0]))[0])
+                u = float(ph.uniforms(seed, b0 + b, j, ph.ACCEPT, np.array([0]))[0])
                 acc = u < rho
                 out["acc_margin"][b, j] = abs(u - rho)
             if not acc:
@@ -287,7 +296,7 @@ def verify(zt, zd, T, F, C, seed, tokens, blk=BLK):
             w = r if np.sum(r) > 0 else p
         else:
             w = p
-        x, mg = gsample(w, seed, b, kstar, ph.BONUS_TOKEN, ph.BONUS_BLOCK, blk)
+        x, mg = gsample(w, seed, b0 + b, kstar, ph.BONUS_TOKEN, ph.BONUS_BLOCK, blk)
         out["bonus"][b] = x
         out["bonus_margin"][b] = mg
     return out

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs (small shapes spanning several blocks and ragged tails,
+every workload at its full size, edge cases)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_verify_sample_amd import workloads as W
+from parity import DTNAME, Report, check_round, raw_host, stats_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+F32, BF16, F16 = torch.float32, torch.bfloat16, torch.float16
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+SMALL = [
+    # B, K, V, dtype, T, F, C, F_out, kind, greedy_half
+    (3, 2, 6, F32, 1.0, 2, 0.5, 2, "normal", False),        # 24-byte rows: unaligned path
+    (2, 3, 1, BF16, 1.0, 0, 1.0, 1, "normal", False),       # V = 1
+    (4, 2, 9, F16, 0.7, 3, 0.3, 5, "normal", False),        # unaligned fp16
+    (2, 4, 2048, BF16, 1.0, 4, 0.5, 4, "normal", False),    # exactly one block
+    (2, 4, 2049, F32, 1.0, 4, 0.5, 8, "normal", False),     # one-element tail block
+    (3, 5, 5000, BF16, 0.9, 4, 0.6, 27, "peaks", False),    # ragged multi-block
+    (4, 3, 20000, F16, 1.3, 8, 0.3, 8, "zipf", True),       # greedy half
+    (1, 0, 3000, BF16, 1.0, 2, 0.5, 2, "normal", False),    # K = 0
+    (2, 7, 40000, BF16, 1.0, 4, 0.5, 64, "normal", False),  # F_out = 64 > NB
+    (4, 3, 16392, F32, 0.5, 4, 1.0, 4, "normal", False),    # C = 1, 8-element tail
+    (3, 2, 70001, BF16, 2.0, 0, 0.5, 0, "normal", False),   # F = 0, odd V
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}K{c[1]}V{c[2]}{DTNAME[c[3]]}")
+def test_small_shapes(case):
+    B, K, V, dt, T, F, C, Fo, kind, gh = case
+    cfg = W.custom(B, K, V, dt, T=T, F=F, C=C, kind=kind, draft_sd=0.7, F_out=Fo, greedy_half=gh)
+    rep = Report()
+    for step in range(6):
+        _say(f"small {cfg.name} step {step}")
+        t, d = W.logits(cfg, step, DEV)
+        r, *_ = check_round(t, d, W.temperatures(cfg, DEV), F, C, W.seed(cfg, step), F_out=Fo, workers=1)
+        rep.add(r)
+    assert rep.ok(), rep.fails
+    _say(f"units {rep.units} near-ties {rep.near}")
+
+
+def test_neg_inf_and_ties():
+    """-inf logits (zero weight), integer-valued logits (many exact ties)."""
+    rep = Report()
+    for step in range(6):
+        g = torch.Generator(device=DEV).manual_seed(100 + step)
+        B, K, V = 3, 4, 7000
+        t = torch.randint(-3, 4, (B, K + 1, V), generator=g, device=DEV).float()
+        d = t + torch.randint(-1, 2, (B, K + 1, V), generator=g, device=DEV).float()
+        mask = torch.rand((B, K + 1, V), generator=g, device=DEV) < 0.3
+        t[mask] = -math.inf
+        d[torch.roll(mask, 1, dims=2)] = -math.inf
+        d[..., 0] = 5.0  # at least one finite entry per draft row
+        t[..., 1] = 5.0
+        for dt in (BF16, F32):
+            T = torch.tensor([1.0, 0.6, 0.0], device=DEV)
+            _say(f"ties step {step} {dt}")
+            r, *_ = check_round(t.to(dt), d.to(dt), T, 3, 0.4, 77 + step, F_out=6, workers=1)
+            rep.add(r)
+    assert rep.ok(), rep.fails
+
+
+def test_topf_tie_overflow_path():
+    """Constant rows: every block ties at the threshold, the candidate list
+    overflows and the exact fallback selection runs."""
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    x = torch.zeros((2, 9000), device=DEV, dtype=BF16)
+    x[1, 4000:] = 1.0
+    idx, val = ssd.topf(x, 5)
+    torch.cuda.synchronize()
+    for r in range(2):
+        oi, ov = O.topf(O.decode(raw_host(x[r]), "bf16"), 5)
+        assert list(idx[r].cpu().numpy()) == list(oi)
+        assert np.array_equal(val[r].cpu().numpy().astype(np.float64), ov)
+
+
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
+def test_softmax_t_and_probs(dt):
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    g = torch.Generator(device=DEV).manual_seed(5)
+    R, V = 7, 33000
+    x = (torch.randn((R, V), generator=g, device=DEV) * 3).to(dt)
+    T = torch.tensor([1.0, 0.5, 0.0, 2.0, 1.3, 0.7, 0.0], device=DEV)
+    st, pr = ssd.softmax_t(x, T, probs=True)
+    torch.cuda.synchronize()
+    lse, mx, am = [a.cpu().numpy() for a in ssd.stats_fields(st)]
+    P = pr.cpu().numpy().astype(np.float64)
+    xr = O.decode(raw_host(x), DTNAME[dt])
+    for r in range(R):
+        o = O.softmax_t(xr[r], float(T[r]))
+        assert mx[r] == o["max"] and am[r] == o["argmax"]
+        assert abs(lse[r] - o["lse"]) <= 1e-5 * max(1, abs(o["lse"]))
+        assert np.all(np.abs(P[r] - o["p"]) <= 1e-5 * o["p"] + 1e-30), r
+
+
+@pytest.mark.parametrize("F", [1, 8, 27, 64])
+def test_topf(F):
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    cfg = W.CONFIGS[2]
+    t, _ = W.logits(W.custom(4, 2, 128256, BF16, kind="peaks"), 0, DEV)
+    x = t.view(-1, t.shape[-1])
+    idx, val = ssd.topf(x, F)
+    torch.cuda.synchronize()
+    xr = O.decode(raw_host(x), "bf16")
+    for r in range(x.shape[0]):
+        oi, ov = O.topf(xr[r], F)
+        assert list(idx[r].cpu().numpy()) == list(oi)
+        assert np.array_equal(val[r].cpu().numpy().astype(np.float64), ov)
+
+
+def test_repeat_calls_are_bit_identical():
+    cfg = W.custom(8, 5, 50000, BF16, kind="zipf")
+    t, d = W.logits(cfg, 0, DEV)
+    T = W.temperatures(cfg, DEV)
+    from parity import gpu_round
+    a = gpu_round(t, d, T, 4, 0.5, 99)
+    b = gpu_round(t, d, T, 4, 0.5, 99)
+    for k in ("tokens", "q", "topf_idx", "topf_val"):
+        assert np.array_equal(a[0][k], b[0][k]), k
+    for k in ("accept_len", "bonus", "p"):
+        assert np.array_equal(a[1][k], b[1][k]), k
+
+
+def test_tiny_verify_workload():
+    """B=1, K=4, V=1000 fp32, T=1, F=2, C=0.5: 250 independent steps."""
+    cfg = W.CONFIGS[1]
+    rep = Report()
+    acc = []
+    for step in range(250):
+        t, d = W.logits(cfg, step, DEV)
+        r, g_s, g_v, *_ = check_round(t, d, W.temperatures(cfg, DEV), cfg.F, cfg.C, W.seed(cfg, step),
+                                      workers=1)
+        rep.add(r)
+        acc.append(int(g_v["accept_len"][0]))
+    _say(f"tiny: units {rep.units} near {rep.near} mean accepted {np.mean(acc):.3f}")
+    assert rep.ok(), rep.fails
+
+
+@pytest.mark.parametrize("c", [2, 3, 4, 5])
+def test_full_size_workload(c):
+    cfg = W.CONFIGS[c]
+    rep = Report()
+    for step in range(2):
+        _say(f"config {c} ({cfg.name}) step {step}: B={cfg.B} K={cfg.K} V={cfg.V}")
+        t, d = W.logits(cfg, step, DEV)
+        r, g_s, g_v, smp, ver, o = check_round(t, d, W.temperatures(cfg, DEV), cfg.F, cfg.C,
+                                               W.seed(cfg, step), F_out=cfg.fout)
+        rep.add(r)
+        _say(f"  units {r.units} near {r.near} fails {len(r.fails)} "
+             f"mean k* {g_v['accept_len'].mean():.3f}")
+        del t, d
+    assert rep.ok(), rep.fails
+
+
+def test_cache_lookup_against_oracle():
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    cfg = W.CONFIGS[4]
+    Fk = ssd.fanout(cfg.Bgt, cfg.K, cfg.ratio, cfg.V)
+    assert Fk == [27, 16, 10, 6, 3, 2]
+    off = O.depth_offsets(Fk)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    B, K = cfg.B, cfg.K
+    topf = torch.stack([torch.randperm(cfg.V, generator=g, device=DEV)[:27 * (K + 1)].view(K + 1, 27)
+                        for _ in range(B)]).to(torch.int32)
+    dev_off = torch.tensor(off, dtype=torch.int32, device=DEV)
+    keys = ssd.cache_keys(topf, dev_off, cfg.Bgt)
+    ok_keys, _ = O.build_keys(topf.cpu().numpy(), Fk)
+    assert np.array_equal(keys.cpu().numpy(), ok_keys)
+    payload = W.payload(cfg, cfg.Bgt, 0, DEV)
+    acc = torch.randint(0, K + 1, (B,), generator=g, device=DEV, dtype=torch.int32)
+    acc[0] = K + 1
+    acc[1] = -1
+    bonus = torch.randint(0, cfg.V, (B,), generator=g, device=DEV, dtype=torch.int32)
+    hits = torch.arange(2, B, 2, device=DEV)
+    kk = acc[hits].clamp(0, K).long()
+    pos = torch.randint(0, 1000, (hits.numel(),), generator=g, device=DEV) % torch.tensor(Fk, device=DEV)[kk]
+    bonus[hits] = topf[hits, kk, pos]
+    hit, slot, toks = ssd.cache_lookup(keys, dev_off, payload, acc, bonus)
+    torch.cuda.synchronize()
+    oh, os_, ot = O.cache_lookup(ok_keys, off, payload.cpu().numpy(), acc.cpu().numpy(), bonus.cpu().numpy())
+    assert np.array_equal(hit.cpu().numpy(), oh)
+    assert np.array_equal(slot.cpu().numpy(), os_)
+    assert np.array_equal(toks.cpu().numpy(), ot)
+    assert oh.sum() >= hits.numel() - 1

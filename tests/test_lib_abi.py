@@ -1,0 +1,126 @@
+"""The C-ABI library: it loads, exports every entry point include/ssd.h
+declares, rejects invalid arguments on the host before any launch, and its
+host-only fan-out matches the oracle bit for bit.  No GPU needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import lossless_verify_sample_amd as ssd
+    if not os.path.exists(ssd.LIB_PATH):
+        from lossless_verify_sample_amd import build
+        build.build(verbose=False)
+    return ssd.library()
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared()
+    assert {"ssd_softmax_t", "ssd_topf", "ssd_saguaro_sample", "ssd_verify", "ssd_cache_lookup",
+            "ssd_cache_keys", "ssd_fanout", "ssd_workspace_bytes", "ssd_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    L.ssd_status_string.restype = ctypes.c_char_p
+    assert L.ssd_status_string(0) == b"SSD_OK"
+    assert L.ssd_status_string(1) == b"SSD_ERR_INVALID_ARG"
+    assert L.ssd_status_string(3) == b"SSD_ERR_WORKSPACE"
+
+
+def test_workspace_sizes(L):
+    import lossless_verify_sample_amd as ssd
+    a = ssd.workspace_bytes(ssd.OP_SAMPLE, 64, 7, 151936)
+    b = ssd.workspace_bytes(ssd.OP_VERIFY, 64, 7, 151936)
+    assert a >= 64 * 8 * 75 * 8 and b > a
+    assert ssd.workspace_bytes(ssd.OP_SAMPLE, 0, 7, 100) == 0
+    assert ssd.workspace_bytes(ssd.OP_SOFTMAX_T, 4, 0, (1 << 20) + 1) == 0
+
+
+def test_fanout_matches_oracle_bit_exact(L):
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    rng = np.random.default_rng(0)
+    cases = [(64, 5, 0.6, 128256), (10, 3, 1.0, 100), (6, 2, 0.5, 2), (7, 0, 0.5, 100), (64, 7, 0.6, 151936)]
+    for _ in range(300):
+        K = int(rng.integers(0, 12))
+        V = int(rng.integers(1, 40))
+        Bgt = int(rng.integers(0, (K + 1) * V + 1))
+        ratio = float(rng.choice([0.5, 0.6, 0.9, 1.0, 1.3, rng.random() * 2 + 1e-3]))
+        cases.append((Bgt, K, ratio, V))
+    for Bgt, K, ratio, V in cases:
+        assert ssd.fanout(Bgt, K, ratio, V) == O.fanout(Bgt, K, ratio, V), (Bgt, K, ratio, V)
+
+
+def test_fanout_rejects_bad_arguments(L):
+    import lossless_verify_sample_amd as ssd
+    for args in ((-1, 3, 0.5, 10), (10, -1, 0.5, 10), (10, 3, 0.0, 10), (10, 3, float("nan"), 10),
+                 (100, 3, 0.5, 10), (10, 33, 0.5, 10)):
+        with pytest.raises(ssd.SSDError):
+            ssd.fanout(*args)
+
+
+def test_entry_points_reject_invalid_arguments_on_host(L):
+    """Each call returns SSD_ERR_INVALID_ARG (1) or SSD_ERR_WORKSPACE (3) before
+    touching the GPU; fake non-null pointers are never dereferenced."""
+    P = ctypes.c_void_p(16)
+    N = None
+    s = L.ssd_softmax_t
+    s.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert s(N, 1, 4, 100, 100, P, P, N, P, 1 << 20, N) == 1          # null logits
+    assert s(P, 7, 4, 100, 100, P, P, N, P, 1 << 20, N) == 1          # bad dtype
+    assert s(P, 1, 4, 100, 99, P, P, N, P, 1 << 20, N) == 1           # ld < V
+    assert s(P, 1, 4, (1 << 20) + 1, 1 << 21, P, P, N, P, 1 << 30, N) == 1  # V too large
+    assert s(P, 1, 4, 100, 100, P, P, N, N, 1 << 20, N) == 3          # no workspace
+    assert s(P, 1, 4, 100, 100, P, P, N, ctypes.c_void_p(256), 8, N) == 3  # too small
+    assert s(P, 1, 4, 100, 100, P, P, N, ctypes.c_void_p(24), 1 << 20, N) == 3  # misaligned
+    t = L.ssd_topf
+    t.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert t(P, 1, 4, 100, 100, 0, P, N, P, 1 << 20, N) == 1          # F = 0
+    assert t(P, 1, 4, 100, 100, 65, P, N, P, 1 << 20, N) == 1         # F > 64
+    assert t(P, 1, 4, 10, 10, 11, P, N, P, 1 << 20, N) == 1           # F > V
+    smp = L.ssd_saguaro_sample
+    smp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_uint64,
+                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    ok = dict(B=2, K=3, V=100, ld=100, F=2, C=0.5, Fo=2)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return smp(P, 1, a["B"], a["K"], a["V"], a["ld"], P, a["F"], a["C"], a["Fo"], 0, P, P, P, P, P, P,
+                   1 << 24, N)
+
+    assert call(C=0.0) == 1 and call(C=1.5) == 1 and call(C=float("nan")) == 1
+    assert call(B=0) == 1 and call(K=-1) == 1 and call(K=33) == 1
+    assert call(Fo=1) == 1            # F_out < F
+    assert call(F=65, Fo=65) == 1
+    v = L.ssd_verify
+    v.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, 1, P, P, P, N, P, 1 << 24, N) == 1  # ld_topf < F
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, N, P, 2, P, P, P, N, P, 1 << 24, N) == 1  # no stats
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, 2, P, P, P, N, P, 16, N) == 3       # small ws
+    lk = L.ssd_cache_lookup
+    lk.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6
+    assert lk(P, N, P, 4, 3, 8, P, P, P, P, P, N) == 1   # no depth offsets
+    assert lk(P, P, P, 0, 3, 8, P, P, P, P, P, N) == 1   # B = 0
