@@ -89,8 +89,8 @@ def main():
         ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=Fo, out=smp_out)
         e[1].record()
         ver_out = dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None)
-        ssd.verify(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["stats"], smp_out["topf_idx"],
-                   out=ver_out)
+        ssd.verify(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["q"], smp_out["stats"],
+                   smp_out["topf_idx"], out=ver_out)
         e[2].record()
         if use_cache:
             keys = ssd.cache_keys(smp_out["topf_idx"], off, a.cache_budget)

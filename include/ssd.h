@@ -147,9 +147,11 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
  * distribution; [SSD-B] part 2: a rejected position's bonus comes from the
  * residual p - q).
  * For j = 0..K-1 in order: rho_j = p_j(x_j) / sigma_j(x_j) with p = softmax of
- * the target row at temperature T and sigma_j rebuilt from the draft row
- * (draft_stats, the first F entries of draft_topf_idx, C); u_j = Philox
- * acceptance draw; accept iff u_j < rho_j; k* = number of leading accepts.
+ * the target row at temperature T and sigma_j(x_j) = draft_q (the draft's own
+ * probability of the token it sampled); u_j = Philox acceptance draw; accept
+ * iff u_j < rho_j; k* = number of leading accepts.  The residual uses the
+ * draft row k* through draft_stats, the first F entries of draft_topf_idx and
+ * C (sigma rebuilt from the draft logits).
  * Bonus: k* < K -> sample the normalised residual max(0, p_k* - sigma_k*)
  * (p_k* if it has no mass); k* = K -> sample p_K.  Greedy sequences: accept
  * iff x_j = argmax of the target row; bonus = argmax of target row k*.
@@ -157,6 +159,8 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
  *   temperature  device float [B]; F, C as used for sampling; seed
  *   draft_tokens device int32 [B, K]; ids outside [0, V) are rejected with
  *                p = 0
+ *   draft_q      device float [B, K]: sigma_j(x_j) from ssd_saguaro_sample
+ *                (a value <= 0 makes rho infinite when p > 0)
  *   draft_stats  device ssd_row_stats [B, K+1] from ssd_saguaro_sample
  *   draft_topf_idx device int32 [B, K+1, ld_topf], ld_topf >= F (NULL if F=0)
  * Outputs (device): out_accept_len int32 [B]; out_bonus int32 [B];
@@ -165,7 +169,7 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
  * workspace: ssd_workspace_bytes(SSD_OP_VERIFY, B, K, V). */
 ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K,
                       int64_t V, int64_t ld, const float* temperature, int32_t F, float C, uint64_t seed,
-                      const int32_t* draft_tokens, const ssd_row_stats* draft_stats,
+                      const int32_t* draft_tokens, const float* draft_q, const ssd_row_stats* draft_stats,
                       const int32_t* draft_topf_idx, int32_t ld_topf, int32_t* out_accept_len,
                       int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, void* workspace,
                       size_t ws_bytes, void* stream);

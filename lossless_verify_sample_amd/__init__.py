@@ -41,8 +41,8 @@ def _load():
         "ssd_topf": [_vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp],
         "ssd_saguaro_sample": [_vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _i32, _u64, _vp, _vp, _vp,
                                _vp, _vp, _vp, _sz, _vp],
-        "ssd_verify": [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _u64, _vp, _vp, _vp, _i32, _vp,
-                       _vp, _vp, _vp, _vp, _sz, _vp],
+        "ssd_verify": [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _u64, _vp, _vp, _vp, _vp, _i32,
+                       _vp, _vp, _vp, _vp, _vp, _sz, _vp],
         "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
@@ -203,7 +203,7 @@ def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None):
     return out
 
 
-def verify(target, draft, temperature, F, C, seed, tokens, draft_stats, draft_topf_idx, want_stats=False,
+def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats, draft_topf_idx, want_stats=False,
            out=None):
     """Acceptance test, accepted length and bonus for target/draft [B, K+1, V].
 
@@ -217,6 +217,7 @@ def verify(target, draft, temperature, F, C, seed, tokens, draft_stats, draft_to
     dev = target.device
     _need(temperature, torch.float32, "temperature", dev)
     _need(tokens, torch.int32, "tokens", dev)
+    _need(draft_q, torch.float32, "draft_q", dev)
     _need(draft_stats, torch.float64, "draft_stats", dev)
     ldf = 0
     if F > 0:
@@ -229,7 +230,7 @@ def verify(target, draft, temperature, F, C, seed, tokens, draft_stats, draft_to
                    stats=_stats_tensor(B * K1, dev) if want_stats else None)
     ws = _workspace(OP_VERIFY, B, K, V, dev)
     _check(_lib.ssd_verify(_p(target), _p(draft), _DT[target.dtype], B, K, V, ld, _p(temperature), F, float(C),
-                           int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_stats),
+                           int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_q), _p(draft_stats),
                            _p(draft_topf_idx) if F > 0 else None, ldf, _p(out["accept_len"]), _p(out["bonus"]),
                            _p(out["p"]), _p(out.get("stats")), _p(ws), ws.numel(), _stream(dev)), "ssd_verify")
     return out

@@ -2,6 +2,7 @@
 // include/ssd.h): host-side argument checks, workspace layout and launches.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "kernels.hpp"
@@ -17,27 +18,35 @@ int64_t nblocks(int64_t V) { return (V + BLK - 1) / BLK; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-  size_t part, cnt, state, rpart, rcnt, total;
+  size_t part, state, rpart, zcap, cand, cst, total;
 };
 
+// Workspace regions (256-byte aligned): block partials of every streamed row;
+// for verification the per-sequence hand-over state, residual block sums and
+// the target logits at the drafted tokens; for sampling and top-F the
+// chunk-local top-F candidates.  Every region is written before it is read
+// within a call, so the workspace needs no initialisation.
 bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   if (n < 1 || V < 1 || V > SSD_MAX_V) return false;
   if ((op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY) && (K < 0 || K > SSD_MAX_K)) return false;
   if (op != SSD_OP_SOFTMAX_T && op != SSD_OP_TOPF && op != SSD_OP_SAMPLE && op != SSD_OP_VERIFY) return false;
   const int64_t NB = nblocks(V);
   const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY) ? n * (K + 1) : n;
-  const int64_t groups = (op == SSD_OP_VERIFY) ? n : rows;
   L->part = 0;
-  L->cnt = al256((size_t)(rows * NB) * sizeof(float2));
-  L->state = L->cnt + al256((size_t)groups * sizeof(unsigned));
+  L->state = L->rpart = L->zcap = L->cand = L->cst = 0;
+  size_t end = al256((size_t)(rows * NB) * sizeof(float2));
   if (op == SSD_OP_VERIFY) {
+    L->state = end;
     L->rpart = L->state + al256((size_t)n * sizeof(SeqState));
-    L->rcnt = L->rpart + al256((size_t)(n * NB) * sizeof(float));
-    L->total = L->rcnt + al256((size_t)n * sizeof(unsigned));
+    L->zcap = L->rpart + al256((size_t)(n * NB) * sizeof(float));
+    end = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
   } else {
-    L->rpart = L->rcnt = 0;
-    L->total = L->state;
+    const int64_t nch = (NB + CH - 1) / CH;
+    L->cand = end;
+    L->cst = L->cand + al256((size_t)(rows * nch * CF) * sizeof(uint64_t));
+    end = L->cst + al256((size_t)(rows * nch) * sizeof(int));
   }
+  L->total = end;
   return true;
 }
 
@@ -53,21 +62,33 @@ hipError_t dispatch(int dt, bool al, A... a) {
   return al ? L<SSD_F16, true>::go(a...) : L<SSD_F16, false>::go(a...);
 }
 
-#define SSD_LAUNCHER(NAME, KERNEL)                                                   \
+#define SSD_LAUNCHER_T(NAME, KERNEL, THREADS)                                         \
   template <int DT, bool AL>                                                         \
   struct NAME {                                                                      \
     static hipError_t go(int64_t grid, const Params& p, hipStream_t st) {            \
-      KERNEL<<<dim3((unsigned)grid), dim3(WG), 0, st>>>(p);                          \
+      KERNEL<<<dim3((unsigned)grid), dim3(THREADS), 0, st>>>(p);                     \
       return hipGetLastError();                                                      \
     }                                                                                \
   };
+#define SSD_LAUNCHER(NAME, KERNEL) SSD_LAUNCHER_T(NAME, KERNEL, WG)
+#define SSD_LAUNCHER_E(NAME, KERNEL) SSD_LAUNCHER_T(NAME, KERNEL, EWG)
 
 SSD_LAUNCHER(LSoftmax, (k_stream<DT, AL, M_SOFTMAX>))
 SSD_LAUNCHER(LTopf, (k_stream<DT, AL, M_TOPF>))
 SSD_LAUNCHER(LSample, (k_stream<DT, AL, M_SAMPLE>))
 SSD_LAUNCHER(LVerify, (k_stream<DT, AL, M_VERIFY>))
+SSD_LAUNCHER_E(LSoftmaxEpi, (k_epi<DT, AL, M_SOFTMAX>))
+SSD_LAUNCHER_E(LTopfEpi, (k_epi<DT, AL, M_TOPF>))
+SSD_LAUNCHER_E(LSampleEpi, (k_epi<DT, AL, M_SAMPLE>))
+SSD_LAUNCHER_E(LVerifyEpi, (k_epi<DT, AL, M_VERIFY>))
 SSD_LAUNCHER(LResidual, (k_residual<DT, AL>))
+SSD_LAUNCHER_E(LResidualEpi, (k_residual_epi<DT, AL>))
 SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
+
+bool local_topf_default() {
+  const char* e = getenv("SSD_LOCAL_TOPF");
+  return e ? atoi(e) != 0 : true;
+}
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
@@ -113,13 +134,13 @@ ssd_status ssd_softmax_t(const void* logits, ssd_dtype dt, int64_t rows, int64_t
   p.temp = temperature;
   char* ws = (char*)workspace;
   p.part = (float2*)(ws + L.part);
-  p.cnt = (unsigned*)(ws + L.cnt);
   p.stats = out_stats;
   p.probs = out_probs;
   const bool al = aligned16(logits, ld, V, dt);
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   hipError_t e = dispatch<LSoftmax>(dt, al, rows * nch, p, st);
+  if (e == hipSuccess) e = dispatch<LSoftmaxEpi>(dt, al, rows, p, st);
   if (e == hipSuccess && out_probs) {
     p.nchunk = (int)cdiv(NB, NWAVE);
     e = dispatch<LProbs>(dt, al, rows * p.nchunk, p, st);
@@ -143,11 +164,16 @@ ssd_status ssd_topf(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, i
   p.F = F; p.F_sel = F;
   char* ws = (char*)workspace;
   p.part = (float2*)(ws + L.part);
-  p.cnt = (unsigned*)(ws + L.cnt);
   p.out_idx = out_idx;
   p.out_val = out_val;
+  p.cand = (uint64_t*)(ws + L.cand);
+  p.cst = (int*)(ws + L.cst);
+  p.local_topf = local_topf_default();
+  const bool al = aligned16(logits, ld, V, dt);
   (void)hipGetLastError();
-  return hip_status(dispatch<LTopf>(dt, aligned16(logits, ld, V, dt), rows * nch, p, (hipStream_t)stream));
+  hipError_t e = dispatch<LTopf>(dt, al, rows * nch, p, (hipStream_t)stream);
+  if (e == hipSuccess) e = dispatch<LTopfEpi>(dt, al, rows, p, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K, int64_t V,
@@ -176,26 +202,31 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
   p.C = C; p.seed = seed;
   char* ws = (char*)workspace;
   p.part = (float2*)(ws + L.part);
-  p.cnt = (unsigned*)(ws + L.cnt);
   p.stats = out_stats;
   p.out_idx = F_out > 0 ? out_topf_idx : nullptr;
   p.out_val = F_out > 0 ? out_topf_val : nullptr;
   p.tokens = out_tokens;
   p.q = out_q;
+  p.cand = (uint64_t*)(ws + L.cand);
+  p.cst = (int*)(ws + L.cst);
+  p.local_topf = local_topf_default();
+  const bool al = aligned16(draft_logits, ld, V, dt);
   (void)hipGetLastError();
-  return hip_status(dispatch<LSample>(dt, aligned16(draft_logits, ld, V, dt), rows * nch, p, (hipStream_t)stream));
+  hipError_t e = dispatch<LSample>(dt, al, rows * nch, p, (hipStream_t)stream);
+  if (e == hipSuccess) e = dispatch<LSampleEpi>(dt, al, rows, p, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K,
                       int64_t V, int64_t ld, const float* temperature, int32_t F, float C, uint64_t seed,
-                      const int32_t* draft_tokens, const ssd_row_stats* draft_stats,
+                      const int32_t* draft_tokens, const float* draft_q, const ssd_row_stats* draft_stats,
                       const int32_t* draft_topf_idx, int32_t ld_topf, int32_t* out_accept_len,
                       int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, void* workspace,
                       size_t ws_bytes, void* stream) {
   if (!target_logits || !draft_logits || !temperature || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
   if (!draft_stats || !out_accept_len || !out_bonus) return SSD_ERR_INVALID_ARG;
   if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
-  if (K > 0 && (!draft_tokens || !out_p)) return SSD_ERR_INVALID_ARG;
+  if (K > 0 && (!draft_tokens || !draft_q || !out_p)) return SSD_ERR_INVALID_ARG;
   if (F < 0 || F > SSD_MAX_F || F > V) return SSD_ERR_INVALID_ARG;
   if (F > 0 && (!draft_topf_idx || ld_topf < F)) return SSD_ERR_INVALID_ARG;
   if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
@@ -214,12 +245,12 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   p.F = F; p.C = C; p.seed = seed;
   char* ws = (char*)workspace;
   p.part = (float2*)(ws + L.part);
-  p.cnt = (unsigned*)(ws + L.cnt);
   p.state = (SeqState*)(ws + L.state);
   p.rpart = (float*)(ws + L.rpart);
-  p.rcnt = (unsigned*)(ws + L.rcnt);
   p.stats = out_target_stats;
   p.dtok = draft_tokens;
+  p.dq = draft_q;
+  p.zcap = (float*)(ws + L.zcap);
   p.dstats = draft_stats;
   p.dtopf = F > 0 ? draft_topf_idx : nullptr;
   p.ld_dtopf = ld_topf;
@@ -230,9 +261,11 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   hipError_t e = dispatch<LVerify>(dt, al, rows * nch, p, st);
-  if (e != hipSuccess) return SSD_ERR_HIP;
+  if (e == hipSuccess) e = dispatch<LVerifyEpi>(dt, al, B, p, st);
   p.nchunk = (int)nchr;
-  return hip_status(dispatch<LResidual>(dt, al, (int64_t)B * nchr, p, st));
+  if (e == hipSuccess) e = dispatch<LResidual>(dt, al, (int64_t)B * nchr, p, st);
+  if (e == hipSuccess) e = dispatch<LResidualEpi>(dt, al, B, p, st);
+  return hip_status(e);
 }
 
 ssd_status ssd_cache_lookup(const int32_t* keys, const int32_t* depth_off, const int32_t* payload, int32_t B,

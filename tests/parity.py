@@ -129,7 +129,8 @@ def gpu_round(target, draft, T, F, C, seed, F_out=None):
     """One sample + verify on the GPU; numpy copies of every output."""
     B, K1, V = draft.shape
     smp = ssd.saguaro_sample(draft, T, F, C, seed, F_out=F_out)
-    ver = ssd.verify(target, draft, T, F, C, seed, smp["tokens"], smp["stats"], smp["topf_idx"], want_stats=True)
+    ver = ssd.verify(target, draft, T, F, C, seed, smp["tokens"], smp["q"], smp["stats"], smp["topf_idx"],
+                     want_stats=True)
     torch.cuda.synchronize()
     g_s = dict(tokens=smp["tokens"].cpu().numpy(), q=smp["q"].cpu().numpy().astype(np.float64),
                stats=stats_np(smp["stats"], B, K1), topf_idx=smp["topf_idx"].cpu().numpy(),
