@@ -13,13 +13,12 @@ namespace ssd {
 constexpr int BLK = SSD_BLOCK;   // vocabulary block (two-level sampler, partials)
 constexpr int WG = 256;          // threads per streaming workgroup
 constexpr int NWAVE = WG / 64;   // wave64s per streaming workgroup
-constexpr int EWG = 512;         // threads per epilogue workgroup (2 waves per SIMD)
+constexpr int EWG = 256;         // threads per epilogue workgroup (one wave per SIMD)
 constexpr int ENW = EWG / 64;
 constexpr int MAX_NB = SSD_MAX_V / SSD_BLOCK;
 constexpr int CAND_CAP = 256;    // top-F candidate list held in LDS
 constexpr int MAX_F = SSD_MAX_F;
 constexpr int MAX_K1 = SSD_MAX_K + 1;
-constexpr int STAGE = 1024;      // partials staged in LDS by the verify epilogue
 
 constexpr double LOG2E = 1.4426950408889634073599246810019;
 constexpr double LN2 = 0.69314718055994530941723212145818;
@@ -131,6 +130,72 @@ __device__ __forceinline__ void load_block(const unsigned char* row, int V, int 
   for (int i = 0; i < 32 / VW; ++i) load_chunk<DT, AL>(row, V, base + i * 64 * VW, &v[i * VW]);
 }
 
+// A block as loaded, still packed: 32-bit words per lane (bf16/fp16 keep two
+// elements per word on the aligned path, half the registers of decoded
+// floats); elements past V hold the bit pattern of -inf.
+template <int DT> struct NegInf;
+template <> struct NegInf<SSD_F32> { static constexpr uint32_t W = 0xFF800000u; };
+template <> struct NegInf<SSD_BF16> { static constexpr uint32_t W = 0xFF80FF80u; static constexpr uint32_t H = 0xFF80u; };
+template <> struct NegInf<SSD_F16> { static constexpr uint32_t W = 0xFC00FC00u; static constexpr uint32_t H = 0xFC00u; };
+
+template <int DT, bool AL>
+struct RawBlock {
+  static constexpr int N = AL ? 8 * Dt<DT>::SZ : 32;
+  uint32_t w[N];
+};
+
+template <int DT, bool AL, bool FULL>
+__device__ __forceinline__ void load_raw(const unsigned char* row, int V, int beta, int lane, RawBlock<DT, AL>& r) {
+  constexpr int VW = Dt<DT>::VW;
+  const int base = beta * BLK + lane * VW;
+  if constexpr (AL) {
+#pragma unroll
+    for (int i = 0; i < 32 / VW; ++i) {
+      const int e0 = base + i * 64 * VW;
+      if constexpr (FULL) {
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + (size_t)e0 * Dt<DT>::SZ));
+        r.w[4 * i] = t.x; r.w[4 * i + 1] = t.y; r.w[4 * i + 2] = t.z; r.w[4 * i + 3] = t.w;
+      } else {
+        const bool in = e0 < V;
+        const uint4 t = *reinterpret_cast<const uint4*>(row + (size_t)(in ? e0 : 0) * Dt<DT>::SZ);
+        r.w[4 * i] = in ? t.x : NegInf<DT>::W;
+        r.w[4 * i + 1] = in ? t.y : NegInf<DT>::W;
+        r.w[4 * i + 2] = in ? t.z : NegInf<DT>::W;
+        r.w[4 * i + 3] = in ? t.w : NegInf<DT>::W;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int e = base + (k / VW) * 64 * VW + (k % VW);
+      const bool in = FULL || e < V;
+      if constexpr (DT == SSD_F32) {
+        const uint32_t x = reinterpret_cast<const uint32_t*>(row)[in ? e : 0];
+        r.w[k] = in ? x : NegInf<DT>::W;
+      } else {
+        const uint32_t x = reinterpret_cast<const uint16_t*>(row)[in ? e : 0];
+        r.w[k] = in ? x : NegInf<DT>::H;
+      }
+    }
+  }
+}
+
+template <int DT, bool AL>
+__device__ __forceinline__ void decode_raw(const RawBlock<DT, AL>& r, float (&v)[32]) {
+  if constexpr (AL) {
+#pragma unroll
+    for (int i = 0; i < 32 / Dt<DT>::VW; ++i)
+      decode16<DT>(make_uint4(r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]), &v[i * Dt<DT>::VW]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if constexpr (DT == SSD_F32) v[k] = __uint_as_float(r.w[k]);
+      else if constexpr (DT == SSD_BF16) v[k] = __uint_as_float(r.w[k] << 16);
+      else v[k] = (float)__builtin_bit_cast(_Float16, (uint16_t)r.w[k]);
+    }
+  }
+}
+
 // Element indices fit in int32 (V <= 2^20).
 template <int DT>
 __device__ __forceinline__ int block_elem_index(int beta, int lane, int k) {
@@ -191,6 +256,21 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp_f<DPP_MIR>(x));
   return fmaxf(fmaxf(rl_f(x, 0), rl_f(x, 16)), fmaxf(rl_f(x, 32), rl_f(x, 48)));
 }
+// Three-input maximum in one instruction (fmaxf would first quiet each
+// operand that does not come from an arithmetic instruction; NaN logits are
+// outside the supported domain).
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float wave_max3(float x) {
+  x = fmax3(x, dpp_f<DPP_XOR1>(x), x);
+  x = fmax3(x, dpp_f<DPP_XOR2>(x), x);
+  x = fmax3(x, dpp_f<DPP_HMIR>(x), x);
+  x = fmax3(x, dpp_f<DPP_MIR>(x), x);
+  return fmax3(fmax3(rl_f(x, 0), rl_f(x, 16), rl_f(x, 32)), rl_f(x, 48), rl_f(x, 48));
+}
 __device__ __forceinline__ float wave_sum(float x) {
   x = x + dpp_f<DPP_XOR1>(x);
   x = x + dpp_f<DPP_XOR2>(x);
@@ -222,86 +302,89 @@ __device__ __forceinline__ int wave_min_i(int x) {
              min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
-// (score desc, index asc) arg-max on doubles.
-struct Arg {
-  double s;
-  int64_t i;
-};
-__device__ __forceinline__ Arg better(Arg a, Arg b) {
-  return (b.s > a.s || (b.s == a.s && b.i < a.i)) ? b : a;
-}
-template <int CTRL>
-__device__ __forceinline__ Arg dpp_arg(Arg a) {
-  return Arg{dpp_d<CTRL>(a.s), (int64_t)dpp_u64<CTRL>((uint64_t)a.i)};
-}
-__device__ __forceinline__ Arg wave_argmax(Arg a) {
-  a = better(a, dpp_arg<DPP_XOR1>(a));
-  a = better(a, dpp_arg<DPP_XOR2>(a));
-  a = better(a, dpp_arg<DPP_HMIR>(a));
-  a = better(a, dpp_arg<DPP_MIR>(a));
-  Arg r0{rl_d(a.s, 0), (int64_t)rl_u64((uint64_t)a.i, 0)};
-  Arg r1{rl_d(a.s, 16), (int64_t)rl_u64((uint64_t)a.i, 16)};
-  Arg r2{rl_d(a.s, 32), (int64_t)rl_u64((uint64_t)a.i, 32)};
-  Arg r3{rl_d(a.s, 48), (int64_t)rl_u64((uint64_t)a.i, 48)};
-  return better(better(r0, r1), better(r2, r3));
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+  x = umin64(x, dpp_u64<DPP_XOR1>(x));
+  x = umin64(x, dpp_u64<DPP_XOR2>(x));
+  x = umin64(x, dpp_u64<DPP_HMIR>(x));
+  x = umin64(x, dpp_u64<DPP_MIR>(x));
+  return umin64(umin64(rl_u64(x, 0), rl_u64(x, 16)), umin64(rl_u64(x, 32), rl_u64(x, 48)));
 }
 
 // ---------------------------------------------------------------------------
 // workgroup reductions for the epilogue kernels (EWG threads; every thread
-// must call and all get the result, combined in a fixed order).  `red` is LDS
-// scratch.
+// calls and gets the result, combined in a fixed order).  Each call site
+// passes its own LDS slot of ENW entries, so one barrier per reduction
+// suffices (a slot is never rewritten within a kernel, or only after a later
+// barrier).
 // ---------------------------------------------------------------------------
-struct Red {
-  double d[ENW];
-  int64_t i[ENW];
-};
-
-__device__ __forceinline__ float wg_max(float x, Red& r) {
+__device__ __forceinline__ float wg_max(float x, float* slot) {
   x = wave_max(x);
-  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.d[w] = x;
-  __syncthreads();
-  float m = (float)r.d[0];
-  for (int k = 1; k < ENW; ++k) m = fmaxf(m, (float)r.d[k]);
+  float m = slot[0];
+#pragma unroll
+  for (int k = 1; k < ENW; ++k) m = fmaxf(m, slot[k]);
   return m;
 }
-__device__ __forceinline__ double wg_sum_d(double x, Red& r) {
+__device__ __forceinline__ double wg_sum_d(double x, double* slot) {
   x = wave_sum_d(x);
-  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.d[w] = x;
-  __syncthreads();
-  double t = 0.0;
-  for (int k = 0; k < ENW; ++k) t += r.d[k];
+  double t = slot[0];
+#pragma unroll
+  for (int k = 1; k < ENW; ++k) t += slot[k];
   return t;
 }
-__device__ __forceinline__ Arg wg_argmax(Arg a, Red& r) {
-  a = wave_argmax(a);
-  const int w = threadIdx.x >> 6;
+__device__ __forceinline__ uint64_t wg_min_u64(uint64_t x, uint64_t* slot) {
+  x = wave_min_u64(x);
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) { r.d[w] = a.s; r.i[w] = a.i; }
-  __syncthreads();
-  Arg b{r.d[0], r.i[0]};
-  for (int k = 1; k < ENW; ++k) b = better(b, Arg{r.d[k], r.i[k]});
-  return b;
-}
-__device__ __forceinline__ uint64_t wg_max_u64(uint64_t x, Red& r) {
-  x = wave_max_u64(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.i[w] = (int64_t)x;
-  __syncthreads();
-  uint64_t m = (uint64_t)r.i[0];
-  for (int k = 1; k < ENW; ++k) m = umax64(m, (uint64_t)r.i[k]);
+  uint64_t m = slot[0];
+#pragma unroll
+  for (int k = 1; k < ENW; ++k) m = umin64(m, slot[k]);
   return m;
 }
+__device__ __forceinline__ uint64_t wg_max_u64(uint64_t x, uint64_t* slot) {
+  x = wave_max_u64(x);
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
+  __syncthreads();
+  uint64_t m = slot[0];
+#pragma unroll
+  for (int k = 1; k < ENW; ++k) m = umax64(m, slot[k]);
+  return m;
+}
+__device__ __forceinline__ int wg_min_i(int x, int* slot) {
+  x = wave_min_i(x);
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
+  __syncthreads();
+  int m = slot[0];
+#pragma unroll
+  for (int k = 1; k < ENW; ++k) m = min(m, slot[k]);
+  return m;
+}
+
+// Race key of a candidate: a non-negative float key (smaller wins) in the
+// high word, its index in the low word, so the unsigned minimum picks the
+// smallest key and, among equal keys, the lowest index.
+__device__ __forceinline__ uint64_t race_key(float key, int idx) {
+  return ((uint64_t)__float_as_uint(key) << 32) | (uint32_t)idx;
+}
+constexpr uint64_t NO_KEY = ~0ull;
 
 // Order-preserving key of (value desc, index asc): larger key = better.
 __device__ __forceinline__ uint64_t vi_key(float v, int64_t idx) {
   uint32_t b = __float_as_uint(v + 0.0f);  // -0 -> +0
   b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+// Order-preserving 32-bit key of a float (larger float, larger key; -0 = +0).
+__device__ __forceinline__ uint32_t ord_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float ord_val(uint32_t b) {
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
 }
 __device__ __forceinline__ float key_val(uint64_t k) {
   uint32_t b = (uint32_t)(k >> 32);
@@ -351,11 +434,8 @@ __device__ __forceinline__ uint32_t draw1(uint64_t seed, uint32_t idx, uint32_t 
 __device__ __forceinline__ float uniform_of(uint32_t w) {
   return (float)(((w >> 9) << 1) | 1u) * 5.9604644775390625e-8f;  // 2^-24
 }
-// g = -ln(-ln u); -ln u from log1p(u - 1) above 1/2 (u - 1 is exact there).
-__device__ __forceinline__ float gumbel_of(uint32_t w) {
-  const float u = uniform_of(w);
-  const float t = u > 0.5f ? -log1pf(u - 1.0f) : -logf(u);
-  return -logf(t);
-}
+// -log2(u) = (-ln u) / ln 2 with the hardware log2 (measured within 1 ulp on
+// gfx950 over every uniform this generator produces, including u near 1).
+__device__ __forceinline__ float neg_log2_u(uint32_t w) { return -__builtin_amdgcn_logf(uniform_of(w)); }
 
 }  // namespace ssd

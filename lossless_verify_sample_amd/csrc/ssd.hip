@@ -18,13 +18,12 @@ int64_t nblocks(int64_t V) { return (V + BLK - 1) / BLK; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-  size_t part, state, rpart, zcap, cand, cst, total;
+  size_t part, state, rpart, zcap, total;
 };
 
 // Workspace regions (256-byte aligned): block partials of every streamed row;
 // for verification the per-sequence hand-over state, residual block sums and
-// the target logits at the drafted tokens; for sampling and top-F the
-// chunk-local top-F candidates.  Every region is written before it is read
+// the target logits at the drafted tokens.  Every region is written before it is read
 // within a call, so the workspace needs no initialisation.
 bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   if (n < 1 || V < 1 || V > SSD_MAX_V) return false;
@@ -33,18 +32,13 @@ bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   const int64_t NB = nblocks(V);
   const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY) ? n * (K + 1) : n;
   L->part = 0;
-  L->state = L->rpart = L->zcap = L->cand = L->cst = 0;
-  size_t end = al256((size_t)(rows * NB) * sizeof(float2));
+  L->state = L->rpart = L->zcap = 0;
+  size_t end = al256((size_t)(rows * NB) * sizeof(float4));
   if (op == SSD_OP_VERIFY) {
     L->state = end;
     L->rpart = L->state + al256((size_t)n * sizeof(SeqState));
     L->zcap = L->rpart + al256((size_t)(n * NB) * sizeof(float));
     end = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
-  } else {
-    const int64_t nch = (NB + CH - 1) / CH;
-    L->cand = end;
-    L->cst = L->cand + al256((size_t)(rows * nch * CF) * sizeof(uint64_t));
-    end = L->cst + al256((size_t)(rows * nch) * sizeof(int));
   }
   L->total = end;
   return true;
@@ -84,11 +78,6 @@ SSD_LAUNCHER_E(LVerifyEpi, (k_epi<DT, AL, M_VERIFY>))
 SSD_LAUNCHER(LResidual, (k_residual<DT, AL>))
 SSD_LAUNCHER_E(LResidualEpi, (k_residual_epi<DT, AL>))
 SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
-
-bool local_topf_default() {
-  const char* e = getenv("SSD_LOCAL_TOPF");
-  return e ? atoi(e) != 0 : true;
-}
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
@@ -133,7 +122,7 @@ ssd_status ssd_softmax_t(const void* logits, ssd_dtype dt, int64_t rows, int64_t
   p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
   p.temp = temperature;
   char* ws = (char*)workspace;
-  p.part = (float2*)(ws + L.part);
+  p.part = (float4*)(ws + L.part);
   p.stats = out_stats;
   p.probs = out_probs;
   const bool al = aligned16(logits, ld, V, dt);
@@ -163,12 +152,9 @@ ssd_status ssd_topf(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, i
   p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
   p.F = F; p.F_sel = F;
   char* ws = (char*)workspace;
-  p.part = (float2*)(ws + L.part);
+  p.part = (float4*)(ws + L.part);
   p.out_idx = out_idx;
   p.out_val = out_val;
-  p.cand = (uint64_t*)(ws + L.cand);
-  p.cst = (int*)(ws + L.cst);
-  p.local_topf = local_topf_default();
   const bool al = aligned16(logits, ld, V, dt);
   (void)hipGetLastError();
   hipError_t e = dispatch<LTopf>(dt, al, rows * nch, p, (hipStream_t)stream);
@@ -201,15 +187,12 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
   p.F = F; p.F_out = F_out; p.F_sel = F_out > 1 ? F_out : 1;
   p.C = C; p.seed = seed;
   char* ws = (char*)workspace;
-  p.part = (float2*)(ws + L.part);
+  p.part = (float4*)(ws + L.part);
   p.stats = out_stats;
   p.out_idx = F_out > 0 ? out_topf_idx : nullptr;
   p.out_val = F_out > 0 ? out_topf_val : nullptr;
   p.tokens = out_tokens;
   p.q = out_q;
-  p.cand = (uint64_t*)(ws + L.cand);
-  p.cst = (int*)(ws + L.cst);
-  p.local_topf = local_topf_default();
   const bool al = aligned16(draft_logits, ld, V, dt);
   (void)hipGetLastError();
   hipError_t e = dispatch<LSample>(dt, al, rows * nch, p, (hipStream_t)stream);
@@ -244,7 +227,7 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   p.temp = temperature;
   p.F = F; p.C = C; p.seed = seed;
   char* ws = (char*)workspace;
-  p.part = (float2*)(ws + L.part);
+  p.part = (float4*)(ws + L.part);
   p.state = (SeqState*)(ws + L.state);
   p.rpart = (float*)(ws + L.rpart);
   p.stats = out_target_stats;
