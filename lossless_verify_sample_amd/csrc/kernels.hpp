@@ -29,6 +29,7 @@ constexpr int CH = 8;             // blocks per workgroup in the streaming pass 
 constexpr int CH_R = 4;           // blocks per workgroup in the residual pass (1 per wave)
 constexpr int TPT = BLK / EWG;    // tokens per epilogue thread in a token stage
 constexpr int NBT = MAX_NB / EWG; // blocks per epilogue thread
+constexpr int NBL = MAX_NB / 64;  // blocks per lane when a wave holds a whole row
 static_assert(TPT == 8 && NBT == 2, "epilogue layout assumes 256 threads over 2048-token blocks");
 
 // What verification hands to the residual pass for one sequence.
@@ -74,7 +75,7 @@ struct Params {
   int32_t* bonus;
   float* p_out;
   SeqState* state;
-  float* rpart;             // residual block sums [B, NB]
+  float2* rpart;            // residual block sums and target block maxima [B, NB]
 };
 
 // LDS of an epilogue workgroup.
@@ -83,17 +84,14 @@ struct ESm {
   double rd[2][ENW];
   uint64_t ru[6][ENW];
   int ri[2][ENW];
-  float M[MAX_NB];          // block maxima of the row
-  float M2[MAX_NB];         // second values of the blocks
-  int I[MAX_NB];            // argmax indices of the blocks
+  float M[MAX_NB];          // block maxima (verification: row K; residual: target row k*)
   float S[MAX_NB];          // block sums (verification: row K)
   int cblk[MAX_NB];         // candidate blocks for top-F
   uint64_t cand[CAND_CAP];  // top-F candidates as (value desc, index asc) keys
+  uint64_t tkey[MAX_F];     // top-F result through LDS, sorted
+  uint64_t wk[ENW][64];     // each wave's own top-F exchange row
   int nre;                  // candidates appended by block re-reads
   int ks;
-  float tval[MAX_F];        // top-F result, sorted
-  int tidx[MAX_F];
-  float es[MAX_F];          // 2^((z_f - m) s) of the top-F set
   float vm[MAX_K1];         // verification, per row j <= K
   double vL[MAX_K1];
   int vfb[MAX_K1];
@@ -213,106 +211,164 @@ __device__ __forceinline__ float block_w(float M, float S, float m, float s) {
 }
 
 // ---------------------------------------------------------------------------
-// epilogue building blocks (EWG threads; thread t owns blocks t + k*EWG)
+// epilogue building blocks.  An epilogue workgroup has ENW waves.  Each wave
+// holds its own copy of a row's partials in registers (block be = lane + 64*i
+// in slot i < PLN), so the row maximum and sum, the top-F threshold and the
+// block draw are computed by every wave without a barrier; the waves split
+// only the 2048-token stage.
 // ---------------------------------------------------------------------------
-// Partials of one row: (M, S) of this thread's blocks into registers, M, M2
-// and I of every block into LDS; also clears the top-F re-read counter.  The
-// caller passes a barrier before LDS is read.
-__device__ __forceinline__ void load_row_partials(const float4* pr, int NB, ESm& sm, float (&M)[NBT],
-                                                  float (&S)[NBT]) {
-  if (threadIdx.x == 0) sm.nre = 0;
-#pragma unroll
-  for (int k = 0; k < NBT; ++k) {
-    const int be = threadIdx.x + k * EWG;
-    const float4 v = be < NB ? pr[be] : make_float4(-INFINITY, 0.f, 0.f, -INFINITY);
-    M[k] = v.x;
-    S[k] = v.y;
-    if (be < NB) {
-      sm.M[be] = v.x;
-      sm.M2[be] = v.w;
-      sm.I[be] = __float_as_int(v.z);
-    }
-  }
-}
+template <int PLN>
+struct WRow {
+  float M[PLN], S[PLN], M2[PLN];
+  int I[PLN];
+};
 
-// Lowest index of value m inside block beta (one wave).
-template <int DT, bool AL>
-__device__ __forceinline__ int wave_first_eq(const unsigned char* rp, int64_t V, int beta, float m) {
+template <int PLN>
+__device__ __forceinline__ void load_wrow(const float4* pr, int NB, WRow<PLN>& r) {
   const int lane = threadIdx.x & 63;
-  float v[32];
-  load_block<DT, AL>(rp, V, beta, lane, v);
-  int best = 0x7fffffff;
 #pragma unroll
-  for (int k = 31; k >= 0; --k) {
-    const int idx = (int)block_elem_index<DT>(beta, lane, k);
-    if (v[k] == m && idx < V) best = min(best, idx);
+  for (int i = 0; i < PLN; ++i) {
+    const int be = lane + 64 * i;
+    const float4 v = be < NB ? pr[be] : make_float4(-INFINITY, 0.f, __int_as_float(-1), -INFINITY);
+    r.M[i] = v.x;
+    r.S[i] = v.y;
+    r.I[i] = __float_as_int(v.z);
+    r.M2[i] = v.w;
   }
-  return wave_min_i(best);
 }
 
-// Exact top-Fs of a row into sm.tval / sm.tidx (value desc, index asc).  The
-// Fs-th largest block maximum tau bounds the Fs-th largest element from
-// below, so every top element lies in a candidate block (maximum >= tau).  A
-// candidate whose second value is below tau holds exactly one element >= tau,
-// its maximum, whose index the partial carries; only the other candidates are
-// re-read, and only their elements >= tau are ranked.  Every wave finds tau
-// itself (a 32-step radix search on ballots over the order-preserving keys of
-// the block maxima), so no barrier precedes the re-reads.  Needs
-// load_row_partials and a barrier since; ends with a barrier.
-template <int DT, bool AL>
-__device__ __forceinline__ void row_topf(const unsigned char* rp, int V, int NB, int Fs, ESm& sm) {
+// Entry be (uniform) of a slot array, read from the lane that holds it.
+template <int PLN, class Tv>
+__device__ __forceinline__ Tv slot_at(const Tv (&x)[PLN], int be) {
+  Tv r = x[0];
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) {
+    const Tv y = __builtin_bit_cast(Tv, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[i]), be & 63));
+    r = (i == (be >> 6)) ? y : r;
+  }
+  return r;
+}
+
+// Low bits of the order-preserving key that only repeat the sign: a bf16
+// value widened to binary32 has 16 zero low bits, an fp16 value 13.
+template <int DT> struct LowBit { static constexpr int B = 0; };
+template <> struct LowBit<SSD_BF16> { static constexpr int B = 16; };
+template <> struct LowBit<SSD_F16> { static constexpr int B = 13; };
+
+// The Fs-th largest of the wave's keys (absent slots hold 0): the largest c
+// with at least Fs keys >= c.  The keys lie in [kmin, kmax], so the answer
+// shares their common high bits; the bits below are found two at a time by
+// counting keys at or above three trial values with ballots.
+template <int PLN>
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&key)[PLN], int Fs, uint32_t kmax, uint32_t kmin,
+                                            int lowbit) {
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0) return kmax;
+  const int hb = 31 - __builtin_clz(diff);
+  uint32_t tk = kmax & ~((2u << hb) - 1u);
+  int bit = hb;
+  for (; bit - 1 >= lowbit; bit -= 2) {
+    const uint32_t c1 = tk | (1u << (bit - 1)), c2 = tk | (2u << (bit - 1)), c3 = tk | (3u << (bit - 1));
+    int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+    for (int i = 0; i < PLN; ++i) {
+      n1 += __popcll(__ballot(key[i] >= c1));
+      n2 += __popcll(__ballot(key[i] >= c2));
+      n3 += __popcll(__ballot(key[i] >= c3));
+    }
+    tk = n3 >= Fs ? c3 : n2 >= Fs ? c2 : n1 >= Fs ? c1 : tk;
+  }
+  if (bit >= lowbit) {
+    const uint32_t c = tk | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < PLN; ++i) n += __popcll(__ballot(key[i] >= c));
+    if (n >= Fs) tk = c;
+  }
+  if (lowbit > 0 && !(tk & 0x80000000u)) tk |= (1u << lowbit) - 1u;  // negative values: low bits all ones
+  return tk;
+}
+
+// Exact top-Fs of a row (value desc, index asc) from a wave's copy of its
+// partials.  tau, the Fs-th largest block maximum, bounds the Fs-th largest
+// element from below, so every top element lies in a candidate block (maximum
+// >= tau).  A candidate whose second value is below tau holds exactly one
+// element >= tau, its maximum, whose index the partial carries.  When every
+// candidate is of that kind (the common case) each wave ranks the candidate
+// maxima itself; otherwise the other candidates are re-read (round-robin
+// over the waves) and all candidates are ranked through LDS.  On return lane
+// r < Fs of every wave holds entry r as a (value, index) key, 0 elsewhere.
+// Every wave of the workgroup calls; sm.nre must have been cleared at start.
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, int NB, int Fs, const WRow<PLN>& r,
+                                              float m, ESm& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int PL = MAX_NB / 64;
-  const int npl = (NB + 63) >> 6;
-  uint32_t key[PL];
+  uint32_t key[PLN];
+  uint32_t kmin = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int be = lane + 64 * i;
-    key[i] = (i < npl && be < NB) ? ord_key(sm.M[be]) : 0u;
+  for (int i = 0; i < PLN; ++i) {
+    const bool in = lane + 64 * i < NB;
+    key[i] = in ? ord_key(r.M[i]) : 0u;
+    kmin = in ? min(kmin, key[i]) : kmin;
   }
-  // tau: the largest key c with at least Fs block maxima at or above it
-  uint32_t tk = 0;
-  if (NB > Fs) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = tk | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (i < npl) cnt += __popcll(__ballot(key[i] >= c));
-      if (cnt >= Fs) tk = c;
-    }
-  }
+  const uint32_t tk = NB > Fs ? kth_key<PLN>(key, Fs, ord_key(m), wave_min_u32(kmin), LowBit<DT>::B) : 0u;
   const float tau = NB > Fs ? ord_val(tk) : -INFINITY;
-  uint64_t cmk[PL], rmk[PL];
-  int n1 = 0;
+  bool cand[PLN], one[PLN];
+  uint64_t more = 0;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int be = lane + 64 * i;
-    const bool c = i < npl && be < NB && key[i] >= tk;
-    cmk[i] = __ballot(c);
-    rmk[i] = __ballot(c && (NB <= Fs || sm.M2[be] >= tau));
-    n1 += __popcll(cmk[i] & ~rmk[i]);
+  for (int i = 0; i < PLN; ++i) {
+    cand[i] = lane + 64 * i < NB && key[i] >= tk;
+    one[i] = cand[i] && NB > Fs && r.M2[i] < tau;
+    more |= __ballot(cand[i] && !one[i]);
   }
-  // wave 0 lists the candidate blocks and the one-element candidates
-  const uint64_t below = (1ull << lane) - 1ull;
-  if (wave == 0) {
-    int nc = 0, k1 = 0;
+  if (more == 0) {
+    uint64_t ck[PLN];
+    int rk[PLN];
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int be = lane + 64 * i;
-      const uint64_t one = cmk[i] & ~rmk[i];
-      if ((cmk[i] >> lane) & 1ull) sm.cblk[nc + __popcll(cmk[i] & below)] = be;
-      if (((one >> lane) & 1ull) && k1 + __popcll(one & below) < CAND_CAP)
-        sm.cand[k1 + __popcll(one & below)] = vi_key(sm.M[be], sm.I[be]);
-      nc += __popcll(cmk[i]);
-      k1 += __popcll(one);
+    for (int i = 0; i < PLN; ++i) {
+      ck[i] = cand[i] ? vi_key(r.M[i], r.I[i]) : 0ull;
+      rk[i] = 0;
     }
-  }
-  // the other candidates are re-read, round-robin over the waves
-  int nr = 0;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    uint64_t rr = rmk[i];
+    for (int i = 0; i < PLN; ++i) {
+      uint64_t mk = __ballot(cand[i]);
+      while (mk) {
+        const uint64_t kc = rl_u64(ck[i], (int)__builtin_ctzll(mk));
+        mk &= mk - 1ull;
+#pragma unroll
+        for (int i2 = 0; i2 < PLN; ++i2) rk[i2] += kc > ck[i2];  // candidates ranked above
+      }
+    }
+    uint64_t* wk = sm.wk[wave];
+#pragma unroll
+    for (int i = 0; i < PLN; ++i)
+      if (cand[i] && rk[i] < Fs) wk[rk[i]] = ck[i];
+    // lanes of one wave exchange through their own LDS rows: LDS executes a
+    // wave's accesses in order; the fences keep the compiler from reordering
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return lane < Fs ? wk[lane] : 0ull;
+  }
+  // general case: wave 0 lists the candidate blocks and the one-element
+  // candidates; the other candidates are re-read round-robin
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  int n1 = 0, ncb = 0, nr = 0;
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) {
+    const int be = lane + 64 * i;
+    const uint64_t cm = __ballot(cand[i]), om = __ballot(one[i]);
+    if (wave == 0) {
+      if (cand[i]) sm.cblk[ncb + __popcll(cm & below)] = be;
+      if (one[i] && n1 + __popcll(om & below) < CAND_CAP) sm.cand[n1 + __popcll(om & below)] = vi_key(r.M[i], r.I[i]);
+    }
+    ncb += __popcll(cm);
+    n1 += __popcll(om);
+  }
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) {
+    uint64_t rr = __ballot(cand[i] && !one[i]);
     while (rr) {
       const int be = 64 * i + (int)__builtin_ctzll(rr);
       rr &= rr - 1ull;
@@ -330,29 +386,25 @@ __device__ __forceinline__ void row_topf(const unsigned char* rp, int V, int NB,
       }
     }
   }
-  int nc = 0;
-#pragma unroll
-  for (int i = 0; i < PL; ++i) nc += __popcll(cmk[i]);
   __syncthreads();
   const int n = n1 + sm.nre;
   if (n <= CAND_CAP) {
-    for (int i = tid; i < n; i += EWG) {
-      const uint64_t ki = sm.cand[i];
-      int r = 0;
-      for (int c = 0; c < n; ++c) r += sm.cand[c] > ki;
-      if (r < Fs) {
-        sm.tval[r] = key_val(ki);
-        sm.tidx[r] = (int)key_idx(ki);
-      }
+    for (int c = tid; c < n; c += EWG) {
+      const uint64_t ki = sm.cand[c];
+      int rk = 0, c2 = 0;
+      for (; c2 + 4 <= n; c2 += 4)
+        rk += (sm.cand[c2] > ki) + (sm.cand[c2 + 1] > ki) + (sm.cand[c2 + 2] > ki) + (sm.cand[c2 + 3] > ki);
+      for (; c2 < n; ++c2) rk += sm.cand[c2] > ki;
+      if (rk < Fs) sm.tkey[rk] = ki;
     }
   } else {
     // Many ties at the threshold: take the best key below the previous one,
     // Fs times, over the candidate blocks (alternating reduction slots).
     uint64_t prev = ~0ull;
     constexpr int VW = Dt<DT>::VW;
-    for (int r = 0; r < Fs; ++r) {
+    for (int rr = 0; rr < Fs; ++rr) {
       uint64_t best = 0;
-      for (int c = wave; c < nc; c += ENW) {
+      for (int c = wave; c < ncb; c += ENW) {
         const int be = sm.cblk[c];
 #pragma unroll 1
         for (int i = 0; i < 32 / VW; ++i) {
@@ -362,28 +414,42 @@ __device__ __forceinline__ void row_topf(const unsigned char* rp, int V, int NB,
 #pragma unroll
           for (int e = 0; e < VW; ++e) {
             if (v[e] >= tau && e0 + e < V) {
-              const uint64_t key = vi_key(v[e], e0 + e);
-              if (key < prev) best = umax64(best, key);
+              const uint64_t kk = vi_key(v[e], e0 + e);
+              if (kk < prev) best = umax64(best, kk);
             }
           }
         }
       }
-      best = wg_max_u64(best, sm.ru[4 + (r & 1)]);
-      if (tid == 0) {
-        sm.tval[r] = key_val(best);
-        sm.tidx[r] = (int)key_idx(best);
-      }
+      best = wg_max_u64(best, sm.ru[4 + (rr & 1)]);
+      if (tid == 0) sm.tkey[rr] = best;
       prev = best;
     }
   }
   __syncthreads();
+  return lane < Fs ? sm.tkey[lane] : 0ull;
 }
 
-// Block stage of the two-level draw: argmin over blocks of -log2(u_be) / W_be
-// (the common factor ln 2 dropped); wfn(be, k) gives W_be >= 0 for the k-th
-// block of this thread.  Returns the chosen block, -1 if no block has mass.
+// Lowest index of value m inside block beta (one wave).
+template <int DT, bool AL>
+__device__ __forceinline__ int wave_first_eq(const unsigned char* rp, int64_t V, int beta, float m) {
+  const int lane = threadIdx.x & 63;
+  float v[32];
+  load_block<DT, AL>(rp, V, beta, lane, v);
+  int best = 0x7fffffff;
+#pragma unroll
+  for (int k = 31; k >= 0; --k) {
+    const int idx = (int)block_elem_index<DT>(beta, lane, k);
+    if (v[k] == m && idx < V) best = min(best, idx);
+  }
+  return wave_min_i(best);
+}
+
+// Block stage over blocks owned by threads (thread t: blocks t + k*EWG):
+// argmin of -log2(u_be) / W_be (the common factor ln 2 dropped); wfn(be)
+// gives W_be >= 0.  Returns the chosen block, -1 if no block has mass.
 template <class WF>
-__device__ int block_stage(int NB, uint64_t seed, int b, int j, uint32_t st, uint64_t* slot, WF wfn) {
+__device__ __forceinline__ int block_stage(int NB, uint64_t seed, int b, int j, uint32_t st, uint64_t* slot,
+                                           WF wfn) {
   uint64_t best = NO_KEY;
 #pragma unroll
   for (int k = 0; k < NBT; ++k) {
@@ -429,7 +495,8 @@ __device__ __forceinline__ void load_run(const unsigned char* rp, int V, int x0,
 // gives the log2 of the inverse weight of token x0 + e up to a constant
 // common to the block (+inf excludes it).  Returns the winner (-1 if none).
 template <class TF>
-__device__ int token_race(int x0, int V, uint64_t seed, int b, int j, uint32_t st, uint64_t* slot, TF tfn) {
+__device__ __forceinline__ int token_race(int x0, int V, uint64_t seed, int b, int j, uint32_t st, uint64_t* slot,
+                                          TF tfn) {
   const uint4 wa = draws4(seed, (uint32_t)(x0 >> 2), (uint32_t)b, (uint32_t)j, st);
   const uint4 wb = draws4(seed, (uint32_t)(x0 >> 2) + 1u, (uint32_t)b, (uint32_t)j, st);
   const uint32_t w[TPT] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
@@ -446,7 +513,16 @@ __device__ int token_race(int x0, int V, uint64_t seed, int b, int j, uint32_t s
   return best == NO_KEY ? -1 : (int)(uint32_t)best;
 }
 
-// Bit e set when token x0 + e is one of idx[0 .. F).
+// Bit e set when token x0 + e is one of the first F entries of a top list
+// held as lane f = entry f (idx), or in memory (ptr).
+__device__ __forceinline__ uint32_t set_mask_lanes(int idx, int F, int x0) {
+  uint32_t msk = 0;
+  for (int f = 0; f < F; ++f) {
+    const uint32_t d = (uint32_t)(__builtin_amdgcn_readlane(idx, f) - x0);
+    if (d < (uint32_t)TPT) msk |= 1u << d;
+  }
+  return msk;
+}
 __device__ __forceinline__ uint32_t set_mask(const int* idx, int F, int x0) {
   uint32_t msk = 0;
   for (int f = 0; f < F; ++f) {
@@ -459,53 +535,59 @@ __device__ __forceinline__ uint32_t set_mask(const int* idx, int F, int x0) {
 // ---------------------------------------------------------------------------
 // epilogues
 // ---------------------------------------------------------------------------
-template <int DT, bool AL>
-__device__ void epi_softmax(const Params& p, int64_t row, ESm& sm) {
-  const int tid = threadIdx.x;
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ void epi_softmax_p(const Params& p, int64_t row) {
+  if (threadIdx.x >= 64) return;  // one wave per row
+  const int lane = threadIdx.x;
   const float T = p.temp[row];
   const bool greedy = !(T > 0.f);
   const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
   const int NB = p.NB;
-  const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
-  float M[NBT], S[NBT];
-  load_row_partials(p.part + row * NB, NB, sm, M, S);
-  const float m = wg_max(fmaxf(M[0], M[1]), sm.rf[0]);
-  int fb = 0x7fffffff;
-  double w = 0.0;
+  WRow<PLN> r;
+  load_wrow<PLN>(p.part + row * NB, NB, r);
+  float lm = r.M[0];
 #pragma unroll
-  for (int k = 0; k < NBT; ++k) {
-    const int be = tid + k * EWG;
-    if (be < NB && M[k] == m) fb = min(fb, be);
-    if (!greedy) w += (double)block_w(M[k], S[k], m, s);
+  for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+  const float m = wave_max(lm);
+  double w = 0.0;
+  int am = -1;
+#pragma unroll
+  for (int i = PLN - 1; i >= 0; --i) {
+    if (!greedy) w += (double)block_w(r.M[i], r.S[i], m, s);
+    const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
+    if (mk) am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));  // first block holding m
   }
-  fb = min(wg_min_i(fb, sm.ri[0]), NB - 1);  // (a NaN row matches no block)
-  const double tot = greedy ? 1.0 : wg_sum_d(w, sm.rd[0]);
-  if (tid == 0) {
+  const double tot = greedy ? 1.0 : wave_sum_d(w);
+  if (lane == 0) {
     ssd_row_stats st;
     st.lse = greedy ? 0.0 : log(tot);
     st.max = m;
-    st.argmax = sm.I[fb];  // the partials carry each block's argmax
+    st.argmax = am < 0 ? 0 : am;  // (a NaN row matches no block)
     p.stats[row] = st;
   }
-  (void)rp;
 }
 
-template <int DT, bool AL>
-__device__ void epi_topf(const Params& p, int64_t row, ESm& sm) {
-  const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
-  float M[NBT], S[NBT];
-  load_row_partials(p.part + row * p.NB, p.NB, sm, M, S);
-  __syncthreads();
-  row_topf<DT, AL>(rp, (int)p.V, p.NB, p.F, sm);
-  for (int r = threadIdx.x; r < p.F; r += EWG) {
-    p.out_idx[row * p.F + r] = sm.tidx[r];
-    if (p.out_val) p.out_val[row * p.F + r] = sm.tval[r];
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ void epi_topf_p(const Params& p, int64_t row, ESm& sm) {
+  if (threadIdx.x == 0) sm.nre = 0;
+  const int NB = p.NB;
+  WRow<PLN> r;
+  load_wrow<PLN>(p.part + row * NB, NB, r);
+  float lm = r.M[0];
+#pragma unroll
+  for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+  const float m = wave_max(lm);
+  const uint64_t tk = wave_topf<DT, AL, PLN>(p.x + row * p.ld * Dt<DT>::SZ, (int)p.V, NB, p.F, r, m, sm);
+  const int lane = threadIdx.x;
+  if (lane < p.F) {  // wave 0 only: lane < F <= 64
+    p.out_idx[row * p.F + lane] = (int)key_idx(tk);
+    if (p.out_val) p.out_val[row * p.F + lane] = key_val(tk);
   }
 }
 
-template <int DT, bool AL>
-__device__ void epi_sample(const Params& p, int64_t row, ESm& sm) {
-  const int tid = threadIdx.x;
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& sm) {
+  const int tid = threadIdx.x, lane = tid & 63;
   const int K1 = p.K + 1;
   const int b = (int)(row / K1), j = (int)(row % K1);
   const float T = p.temp[b];
@@ -514,58 +596,83 @@ __device__ void epi_sample(const Params& p, int64_t row, ESm& sm) {
   const int NB = p.NB, V = (int)p.V, F = p.F;
   const float C = p.C;
   const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
-  float M[NBT], S[NBT];
-  load_row_partials(p.part + row * NB, NB, sm, M, S);
-  const float m = wg_max(fmaxf(M[0], M[1]), sm.rf[0]);
-  float w[NBT];
-  double wsum = 0.0;
+  if (tid == 0) sm.nre = 0;
+  const bool draw = !greedy && j < p.K;
+  // -log2(u) of every block for the block stage: independent of the logits,
+  // computed while the partials load
+  float E[PLN];
 #pragma unroll
-  for (int k = 0; k < NBT; ++k) {
-    w[k] = greedy ? 0.f : block_w(M[k], S[k], m, s);
-    wsum += (double)w[k];
+  for (int i = 0; i < PLN; ++i)
+    E[i] = draw ? neg_log2_u(draw1(p.seed, (uint32_t)(lane + 64 * i), (uint32_t)b, (uint32_t)j, ST_DRAFT_BLOCK))
+                : 0.f;
+  WRow<PLN> r;
+  load_wrow<PLN>(p.part + row * NB, NB, r);
+  float lm = r.M[0];
+#pragma unroll
+  for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+  const float m = wave_max(lm);
+  float w[PLN];
+  double ws = 0.0;
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) {
+    w[i] = greedy ? 0.f : block_w(r.M[i], r.S[i], m, s);
+    ws += (double)w[i];
   }
-  const double tot0 = greedy ? 1.0 : wg_sum_d(wsum, sm.rd[0]);
-  row_topf<DT, AL>(rp, V, NB, p.F_sel, sm);
-  // sigma_{F,C}: the first F of the top list form S; their weights
-  if (!greedy && tid < F) sm.es[tid] = __builtin_amdgcn_exp2f((sm.tval[tid] - m) * s);
-  __syncthreads();
-  auto row_lse = [&]() -> double {  // ln of the sigma normaliser, relative to m
-    double zs = 0.0;
-    for (int f = 0; f < F; ++f) zs += (double)sm.es[f];
-    return log((tot0 - zs) + (double)C * zs);
-  };
-  if (tid == 0) {
-    ssd_row_stats st;
-    st.lse = greedy ? 0.0 : row_lse();
-    st.max = m;
-    st.argmax = sm.tidx[0];
-    p.stats[row] = st;
-  }
-  for (int r = tid; r < p.F_out; r += EWG) {
-    if (p.out_idx) p.out_idx[row * p.F_out + r] = sm.tidx[r];
-    if (p.out_val) p.out_val[row * p.F_out + r] = sm.tval[r];
+  const double tot0 = greedy ? 1.0 : wave_sum_d(ws);
+  const uint64_t tkey = wave_topf<DT, AL, PLN>(rp, V, NB, p.F_sel, r, m, sm);
+  const float tv = key_val(tkey);
+  const int ti = (int)key_idx(tkey);
+  // sigma_{F,C}: lane f < F holds 2^((z_f - m) s) of the f-th member of S
+  const float es = (!greedy && lane < F) ? __builtin_amdgcn_exp2f((tv - m) * s) : 0.f;
+  const double zs = wave_sum_d((double)es);
+  const double lse = greedy ? 0.0 : log((tot0 - zs) + (double)C * zs);
+  if (tid < 64) {
+    if (lane < p.F_out) {
+      if (p.out_idx) p.out_idx[row * p.F_out + lane] = ti;
+      if (p.out_val) p.out_val[row * p.F_out + lane] = tv;
+    }
+    if (lane == 0) {
+      ssd_row_stats st;
+      st.lse = lse;
+      st.max = m;
+      st.argmax = ti;
+      p.stats[row] = st;
+    }
   }
   if (j == p.K) return;  // row K only predicts the bonus after K acceptances
   if (greedy) {
     if (tid == 0) {
-      p.tokens[b * p.K + j] = sm.tidx[0];
+      p.tokens[b * p.K + j] = ti;
       p.q[b * p.K + j] = 1.0f;
     }
     return;
   }
-  int beta = block_stage(NB, p.seed, b, j, ST_DRAFT_BLOCK, sm.ru[0], [&](int be, int k) -> float {
-    float corr = 0.f;
-    for (int f = 0; f < F; ++f)
-      if (sm.tidx[f] / BLK == be) corr += sm.es[f];
-    return corr > 0.f ? fmaxf(w[k] - corr, 0.f) + C * corr : w[k];
-  });
-  if (beta < 0) beta = 0;  // no block of mass only for invalid rows
+  // block stage (every wave): blocks holding members of S lose (1 - C) of
+  // those members' weight
+  float corr[PLN];
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) corr[i] = 0.f;
+  for (int f = 0; f < F; ++f) {
+    const int bf = __builtin_amdgcn_readlane(ti, f) / BLK;
+    const float ef = rl_f(es, f);
+#pragma unroll
+    for (int i = 0; i < PLN; ++i) corr[i] += (bf == lane + 64 * i) ? ef : 0.f;
+  }
+  uint64_t bk = NO_KEY;
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) {
+    const float W = corr[i] > 0.f ? fmaxf(w[i] - corr[i], 0.f) + C * corr[i] : w[i];
+    if (lane + 64 * i < NB && W > 0.f) bk = umin64(bk, race_key(E[i] * __builtin_amdgcn_rcpf(W), lane + 64 * i));
+  }
+  bk = wave_min_u64(bk);
+  const int beta = bk == NO_KEY ? 0 : (int)(uint32_t)bk;  // no block of mass only for invalid rows
+  // token stage over block beta
   const int x0 = beta * BLK + TPT * tid;
   float z[TPT];
   load_run<DT, AL>(rp, V, x0, z);
-  const uint32_t smask = set_mask(sm.tidx, F, x0);
+  const uint32_t smask = set_mask_lanes(ti, F, x0);
   const float nc2 = -__builtin_amdgcn_logf(C);  // -log2 C >= 0
-  const float Mb = sm.M[beta];
+  const float Mb = slot_at<PLN>(r.M, beta);
   const int x = token_race(x0, V, p.seed, b, j, ST_DRAFT_TOKEN, sm.ru[1], [&](int e) -> float {
     if (!(z[e] > -INFINITY)) return INFINITY;
     return (Mb - z[e]) * s + (((smask >> e) & 1u) ? nc2 : 0.f);
@@ -577,17 +684,17 @@ __device__ void epi_sample(const Params& p, int64_t row, ESm& sm) {
 #pragma unroll
     for (int e = 1; e < TPT; ++e) zx = (d == (uint32_t)e) ? z[e] : zx;
     const bool inS = (smask >> d) & 1u;
-    const double lq = ((double)zx - (double)m) * (1.0 / (double)T) + (inS ? log((double)C) : 0.0) - row_lse();
+    const double lq = ((double)zx - (double)m) * (1.0 / (double)T) + (inS ? log((double)C) : 0.0) - lse;
     p.tokens[b * p.K + j] = x;
-    p.q[b * p.K + j] = (float)exp(lq);
+    p.q[b * p.K + j] = __builtin_amdgcn_exp2f((float)(lq * LOG2E));
   } else if (x < 0 && tid == 0) {
     p.tokens[b * p.K + j] = 0;
     p.q[b * p.K + j] = 0.f;
   }
 }
 
-template <int DT, bool AL>
-__device__ void epi_verify(const Params& p, int b, ESm& sm) {
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
   const int K = p.K, K1 = K + 1, NB = p.NB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int V = (int)p.V;
@@ -612,48 +719,49 @@ __device__ void epi_verify(const Params& p, int b, ESm& sm) {
     dmax = ds.max;
     dlse = ds.lse;
   }
-  // row statistics: wave w merges rows j = w, w + ENW, ...
-  constexpr int PL = MAX_NB / 64;
-  for (int j = wave; j < K1; j += ENW) {
-    const float4* pr = p.part + (r0 + j) * NB;
-    float Mv[PL], Sv[PL];
+  // row statistics: wave w merges rows j = w, w + ENW, ..., two rows per pass
+  // with both rows' loads in flight
+  auto merge = [&](const WRow<PLN>& r, int j) {
+    float lm = r.M[0];
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int be = lane + 64 * i;
-      const float4 v = be < NB ? pr[be] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
-      Mv[i] = v.x;
-      Sv[i] = v.y;
-    }
-    float lm = Mv[0];
-#pragma unroll
-    for (int i = 1; i < PL; ++i) lm = fmaxf(lm, Mv[i]);
+    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
     const float m = wave_max(lm);
-    int fb = 0x7fffffff;
+    int fb = -1, am = -1;
     double wsum = 0.0;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      if (Mv[i] == m) fb = min(fb, lane + 64 * i);
-      if (!greedy) wsum += (double)block_w(Mv[i], Sv[i], m, s);
+    for (int i = PLN - 1; i >= 0; --i) {
+      if (!greedy) wsum += (double)block_w(r.M[i], r.S[i], m, s);
+      const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
+      if (mk) {
+        fb = 64 * i + (int)__builtin_ctzll(mk);
+        am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
+      }
     }
-    fb = min(wave_min_i(fb), NB - 1);
     wsum = wave_sum_d(wsum);
     if (j == K) {
 #pragma unroll
-      for (int i = 0; i < PL; ++i) {
+      for (int i = 0; i < PLN; ++i) {
         const int be = lane + 64 * i;
         if (be < NB) {
-          sm.M[be] = Mv[i];
-          sm.S[be] = Sv[i];
+          sm.M[be] = r.M[i];
+          sm.S[be] = r.S[i];
         }
       }
     }
     if (lane == 0) {
       sm.vm[j] = m;
       sm.vL[j] = greedy ? 0.0 : log(wsum);
-      sm.vfb[j] = fb;
-      // greedy rows carry the block argmax in their partial
-      sm.vam[j] = greedy ? __float_as_int(pr[fb].z) : -1;
+      sm.vfb[j] = fb < 0 ? 0 : fb;      // (a NaN row matches no block)
+      sm.vam[j] = greedy ? (am < 0 ? 0 : am) : -1;  // greedy rows carry the block argmax in their partial
     }
+  };
+  for (int j0 = wave; j0 < K1; j0 += 2 * ENW) {
+    const int j1 = j0 + ENW;
+    WRow<PLN> ra, rb;
+    load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
+    load_wrow<PLN>(p.part + (r0 + min(j1, K)) * NB, NB, rb);
+    merge(ra, j0);
+    if (j1 < K1) merge(rb, j1);
   }
   __syncthreads();
   // argmax of the T > 0 rows is only needed for the optional statistics
@@ -739,22 +847,33 @@ __device__ void epi_verify(const Params& p, int b, ESm& sm) {
 }
 
 template <int DT, bool AL>
-__device__ void epi_residual(const Params& p, int b, const SeqState& ss, ESm& sm) {
+__device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqState& ss, ESm& sm) {
   const int tid = threadIdx.x, K1 = p.K + 1, NB = p.NB, ks = ss.kstar, V = (int)p.V, F = p.F;
   const int64_t row = (int64_t)b * K1 + ks;
   const int64_t rs = p.ld * Dt<DT>::SZ;
   const unsigned char* rt = p.x + row * rs;
   const unsigned char* rd = p.xd + row * rs;
   const float s = ss.s, mt = ss.m_t;
-  // residual block sums; target row k*'s partials for the no-residual case
-  float R[NBT], M[NBT], S[NBT];
-  load_row_partials(p.part + row * NB, NB, sm, M, S);
+  // residual block sums with the target row's block maxima
+  float R[NBT];
 #pragma unroll
   for (int k = 0; k < NBT; ++k) {
     const int be = tid + k * EWG;
-    R[k] = be < NB ? p.rpart[(int64_t)b * NB + be] : 0.f;
+    const float2 v = be < NB ? p.rpart[(int64_t)b * NB + be] : make_float2(0.f, -INFINITY);
+    R[k] = v.x;
+    if (be < NB) sm.M[be] = v.y;
   }
   const int any = __syncthreads_or(R[0] > 0.f || R[1] > 0.f);
+  float M[NBT], S[NBT];
+  if (!any) {  // no residual mass: p_k* from the target row's partials
+#pragma unroll
+    for (int k = 0; k < NBT; ++k) {
+      const int be = tid + k * EWG;
+      const float4 v = be < NB ? p.part[row * NB + be] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+      M[k] = v.x;
+      S[k] = v.y;
+    }
+  }
   int beta = block_stage(NB, p.seed, b, ks, ST_BONUS_BLOCK, sm.ru[0], [&](int, int k) -> float {
     return any ? R[k] : block_w(M[k], S[k], mt, s);
   });
@@ -840,10 +959,12 @@ template <int DT, bool AL, int MODE>
 __global__ __launch_bounds__(EWG) void k_epi(Params p) {
   __shared__ ESm sm;
   const int g = blockIdx.x;
-  if constexpr (MODE == M_VERIFY) epi_verify<DT, AL>(p, g, sm);
-  if constexpr (MODE == M_SOFTMAX) epi_softmax<DT, AL>(p, g, sm);
-  if constexpr (MODE == M_TOPF) epi_topf<DT, AL>(p, g, sm);
-  if constexpr (MODE == M_SAMPLE) epi_sample<DT, AL>(p, g, sm);
+  // rows of up to 128 blocks (V <= 262144) keep two partials per lane
+  const bool small = p.NB <= 128;
+  if constexpr (MODE == M_VERIFY) small ? epi_verify_p<DT, AL, 2>(p, g, sm) : epi_verify_p<DT, AL, NBL>(p, g, sm);
+  if constexpr (MODE == M_SOFTMAX) small ? epi_softmax_p<DT, AL, 2>(p, g) : epi_softmax_p<DT, AL, NBL>(p, g);
+  if constexpr (MODE == M_TOPF) small ? epi_topf_p<DT, AL, 2>(p, g, sm) : epi_topf_p<DT, AL, NBL>(p, g, sm);
+  if constexpr (MODE == M_SAMPLE) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
 }
 
 // Residual pass for sequences rejected at k* < K: block sums of
@@ -874,6 +995,10 @@ __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 5) void k_residual
     load_block<DT, AL>(rd, V, be, lane, vd);
   }
   const float s = ss.s, ot = ss.o_t, od = ss.o_d, nk = -ss.kf;
+  float g[32 / Dt<DT>::VW];
+#pragma unroll
+  for (int i = 0; i < 32 / Dt<DT>::VW; ++i) g[i] = group_max<Dt<DT>::VW>(&vt[i * Dt<DT>::VW]);
+  const float Mt = wave_max3(lane_max<32 / Dt<DT>::VW>(g));
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int k = 0; k < 32; k += 2) {
@@ -895,7 +1020,7 @@ __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 5) void k_residual
       R += fmaxf(fmaf(nk * p.C, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
     }
   }
-  if (lane == 0) p.rpart[(int64_t)b * p.NB + be] = fmaxf(R, 0.f);
+  if (lane == 0) p.rpart[(int64_t)b * p.NB + be] = make_float2(fmaxf(R, 0.f), Mt);
 }
 
 template <int DT, bool AL>

@@ -37,7 +37,7 @@ bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   if (op == SSD_OP_VERIFY) {
     L->state = end;
     L->rpart = L->state + al256((size_t)n * sizeof(SeqState));
-    L->zcap = L->rpart + al256((size_t)(n * NB) * sizeof(float));
+    L->zcap = L->rpart + al256((size_t)(n * NB) * sizeof(float2));
     end = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
   }
   L->total = end;
@@ -229,7 +229,7 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   char* ws = (char*)workspace;
   p.part = (float4*)(ws + L.part);
   p.state = (SeqState*)(ws + L.state);
-  p.rpart = (float*)(ws + L.rpart);
+  p.rpart = (float2*)(ws + L.rpart);
   p.stats = out_target_stats;
   p.dtok = draft_tokens;
   p.dq = draft_q;
