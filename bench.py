@@ -9,9 +9,21 @@ V=151936 (Qwen-3 vocabulary), bf16 logits, T=1, F=4, C=0.5; cache budget 64
 with fan-out ratio 0.6.  Inputs rotate over > 1 GiB of distinct sets so the
 256 MB Infinity Cache cannot serve them.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--config N] [--no-cache] [--no-cpu-baseline]
+  python bench.py --copy-gib G   (plain device copy of G GiB, for counter calibration)
+
+Roofline: the dominant kernel is the streaming pass (one read of every logit
+row) of sampling or verification, whichever takes longer.  After the timed
+steps the same steps run once more with the library's kernel timer on, which
+stamps each streaming launch with HIP events recorded by the launch itself on
+the call's stream (a separate pass because the event work slows the step).  Algorithmic bytes per launch = B (K+1) V element
+bytes read + one 16-byte partial per 2048-token block written (+ the drafted
+tokens and captured target logits for verification).  `traffic` comes from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary committed under profiles/ for that
+kernel, and is null when the kernel sources changed since it was taken.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -35,7 +47,54 @@ def parse():
     ap.add_argument("--no-cache", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-input-gib", type=float, default=1.1)
+    ap.add_argument("--copy-gib", type=float, default=0.0)
     return ap.parse_args()
+
+
+def source_hash():
+    """sha256 (16 hex digits) of the kernel sources."""
+    h = hashlib.sha256()
+    for f in ("device.hpp", "kernels.hpp", "ssd.hip"):
+        with open(os.path.join(ROOT, "lossless_verify_sample_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from its committed counter summary
+    (profiles/*.md line 'traffic: kernel=... source=... fetch_bytes=...
+    write_bytes=...'), if it was taken on the current sources."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    for f in sorted(os.listdir(pdir)):
+        if not f.endswith(".md"):
+            continue
+        for line in open(os.path.join(pdir, f)):
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split()[1:])
+            if kv.get("kernel") == kernel and kv.get("source") == source_hash():
+                return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    return None
+
+
+def copy_calibration(gib):
+    """A plain device-to-device copy of `gib` GiB, timed: the reference for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = int(gib * 2 ** 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "seconds": el,
+                      "gbs": round(2 * n * 4 / el / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -44,6 +103,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a design "
                                    "note, not an implementation", "n_gpus": a.gpus}), flush=True)
         sys.exit(2)
+    if a.copy_gib > 0:
+        copy_calibration(a.copy_gib)
+        return
     import torch
 
     import lossless_verify_sample_amd as ssd
@@ -81,23 +143,27 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
     hit_list = []
 
-    def step(i):
+    def step(i, instrument=False):
         t, d = sets[i % nsets]
         seed = W.seed(cfg, i)
-        e = ev[i]
-        e[0].record()
+        e = ev[i] if instrument else None
+        if e:
+            e[0].record()
         ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=Fo, out=smp_out)
-        e[1].record()
+        if e:
+            e[1].record()
         ver_out = dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None)
         ssd.verify(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["q"], smp_out["stats"],
                    smp_out["topf_idx"], out=ver_out)
-        e[2].record()
+        if e:
+            e[2].record()
         if use_cache:
             keys = ssd.cache_keys(smp_out["topf_idx"], off, a.cache_budget)
             h, _, _ = ssd.cache_lookup(keys, off, payloads[i % nsets], acc_buf[i], bonus)
-            if i >= a.warmup:
+            if not instrument and i >= a.warmup:
                 hit_list.append(h)
-        e[3].record()
+        if e:
+            e[3].record()
 
     for i in range(a.warmup):
         step(i)
@@ -108,6 +174,15 @@ def main():
         step(i)
     stop.record()
     torch.cuda.synchronize()
+    # instrumented pass: the same steps again with per-call events and the
+    # streaming launches stamped by their own events (kept out of the headline
+    # pass, whose step time the event work would inflate)
+    ssd.timer_enable(a.steps)
+    for i in range(a.warmup, total):
+        step(i, instrument=True)
+    torch.cuda.synchronize()
+    k_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
+    ssd.timer_enable(0)
     ms = start.elapsed_time(stop) / a.steps
     timed = range(a.warmup, total)
     t_s = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed) / a.steps
@@ -123,8 +198,16 @@ def main():
     rows_per_s = cfg.rows / (ms * 1e-3)
     gbs_sample = b_sample / (t_s * 1e-3) / 1e9
     gbs_verify = b_verify / (t_v * 1e-3) / 1e9
-    dominant = "sample" if t_s >= t_v else "verify"
-    achieved = gbs_sample if dominant == "sample" else gbs_verify
+    # the dominant kernel: the longer of the two streaming passes
+    k_ms = {op: (t / n if n else float("nan")) for op, (n, t) in k_launch.items()}
+    NB = -(-V // 2048)
+    k_bytes = {ssd.OP_SAMPLE: cfg.rows * row_bytes + cfg.rows * NB * 16,
+               ssd.OP_VERIFY: cfg.rows * row_bytes + cfg.rows * NB * 16 + 2 * B * K * 4 + B * K * 4}
+    dom = ssd.OP_SAMPLE if k_ms[ssd.OP_SAMPLE] >= k_ms[ssd.OP_VERIFY] else ssd.OP_VERIFY
+    dtn = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[cfg.dtype]
+    kname = f"k_stream<{dtn},aligned,{'sample' if dom == ssd.OP_SAMPLE else 'verify'}>"
+    achieved = k_bytes[dom] / (k_ms[dom] * 1e-3) / 1e9
+    traffic = recorded_traffic(kname)
     out = {
         "metric": "verified logit rows/s",
         "value": round(rows_per_s, 1),
@@ -152,39 +235,52 @@ def main():
         "gbs_verify": round(gbs_verify, 1),
         "cache_hit_rate": round(float(torch.stack(hit_list).sum().item()) / (a.steps * B), 4) if use_cache else None,
         "roofline": {
-            "kernel": "k_stream<bf16,aligned,sample>" if dominant == "sample" else "ssd_verify (target pass + residual pass)",
+            "kernel": kname,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "algorithmic_bytes": k_bytes[dom],
+            "launches": k_launch[dom][0],
+            "ms_per_launch": round(k_ms[dom], 5),
+            "source": source_hash(),
         },
+        "ms_stream_sample": round(k_ms[ssd.OP_SAMPLE], 5),
+        "ms_stream_verify": round(k_ms[ssd.OP_VERIFY], 5),
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, sets[0], T, Fo)
+        out["cpu_baseline"] = cpu_baseline(cfg, sets, T, Fo)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, tset, T, Fo):
-    """The oracle (unchanged) on one full step of the workload on the host cores."""
+def cpu_baseline(cfg, sets, T, Fo, min_seconds=10.0, max_steps=64):
+    """The oracle (unchanged) on whole steps of the workload on the host
+    cores: sample + verify of every row, repeated over the input sets until
+    about min_seconds have passed."""
     import numpy as np
     import torch
 
     from oracle import pool as OP
-    t, d = tset
 
     def raw(x):
         return x.view(torch.int16).cpu().numpy().view(np.uint16) if x.dtype != torch.float32 else x.cpu().numpy()
 
     dt = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[cfg.dtype]
-    rt, rd = raw(t), raw(d)
+    Th = T.cpu().numpy().astype(np.float64)
+    host = [(raw(t), raw(d)) for t, d in sets]
     workers = OP.default_workers()
     t0 = time.perf_counter()
-    OP.run(rd, dt, T.cpu().numpy().astype(np.float64), cfg.F, cfg.C, 0, F_out=Fo, target_raw=rt, workers=workers)
+    n = 0
+    while n < max_steps and (n == 0 or time.perf_counter() - t0 < min_seconds):
+        rt, rd = host[n % len(host)]
+        OP.run(rd, dt, Th, cfg.F, cfg.C, n, F_out=Fo, target_raw=rt, workers=workers)
+        n += 1
     el = time.perf_counter() - t0
-    return {"value": round(cfg.rows / el, 2), "unit": "rows/s", "cores": workers, "kind": "oracle",
-            "sample": f"one full step ({cfg.B} sequences, {cfg.rows} rows: sample + verify), {el:.1f} s wall"}
+    return {"value": round(n * cfg.rows / el, 2), "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n} full steps ({cfg.B} sequences, {cfg.rows} rows each: sample + verify) "
+                      f"in {el:.1f} s wall"}
 
 
 if __name__ == "__main__":

@@ -23,7 +23,8 @@
  *   Entries must be finite or -inf (weight zero); each row needs one finite
  *   entry.  NaN and +inf are not supported.
  * - Pointers named "device" are HIP device memory owned by the caller; the
- *   library allocates nothing and keeps no state between calls.
+ *   library allocates no device memory and keeps no state between calls
+ *   (the optional kernel timer below aside).
  * - `stream` is a hipStream_t (NULL = default stream).  Every call is
  *   asynchronous: it validates its scalar arguments, enqueues its kernels
  *   and returns; nothing synchronises inside the library.
@@ -38,10 +39,10 @@
  *   randomness).
  * - Ties (argmax, top-F order, Gumbel scores) go to the lowest index.
  * - Workspace: a device buffer of at least ssd_workspace_bytes(...) bytes,
- *   16-byte aligned, ZERO-FILLED before its first use.  Each call leaves its
- *   internal counters at zero again, so the buffer can be reused by later
- *   calls of the same op without clearing.  Calls that share a workspace
- *   must not overlap in time (use one stream or one workspace per stream).
+ *   256-byte aligned, contents irrelevant: every call writes each region
+ *   before reading it.  It holds per-block partials between the kernels of
+ *   one call, so calls that share a workspace must not overlap in time (use
+ *   one stream or one workspace per stream).
  * - Randomness: key = (seed & 0xffffffff, seed >> 32); counter =
  *   (idx >> 2, b, j, stream id); the draw is output word idx & 3, with idx the
  *   token id (token streams), the 2048-token block id (block streams) or 0
@@ -50,7 +51,9 @@
  *   0.5) * 2^-23; Gumbel g = -ln(-ln u).
  * - Sampling from weights w uses the exact two-level Gumbel-max rule over
  *   2048-token blocks: block beta* = argmax ln W_beta + g(beta) over blocks of
- *   nonzero mass, then token = argmax ln w_x + g(x) inside beta*.
+ *   nonzero mass, then token = argmax ln w_x + g(x) inside beta*.  The
+ *   kernels evaluate each argmax in the equivalent form argmin (-ln u) / w
+ *   (g = -ln(-ln u) is decreasing in -ln u), in binary32.
  */
 #ifndef SSD_H
 #define SSD_H
@@ -215,6 +218,22 @@ size_t ssd_workspace_bytes(ssd_op op, int64_t n, int32_t K, int64_t V);
 
 /* Static string naming a status. */
 const char* ssd_status_string(ssd_status s);
+
+/* Kernel timer, a measurement aid (not part of the method).  While enabled,
+ * every launch of the streaming pass -- the kernel that reads each logit row
+ * once from HBM, in ssd_softmax_t, ssd_topf, ssd_saguaro_sample and
+ * ssd_verify -- is timed by a pair of HIP events that the launch itself
+ * records on the call's stream (hipExtLaunchKernelGGL), up to max_launches
+ * launches per op.
+ *   ssd_timer_enable(n): n > 0 (re)creates the events and clears the counts;
+ *     n = 0 destroys them.  Host-side state of the library, not thread-safe:
+ *     enable, read and disable from one thread while no call is in flight.
+ *     Errors: n < 0 or n > 1 << 20 (INVALID_ARG), event creation (HIP).
+ *   ssd_timer_read(op, &launches, &total_ms): waits for the recorded events
+ *     and returns how many launches of that op were timed and their summed
+ *     duration in milliseconds.  Errors: bad op or null pointers. */
+ssd_status ssd_timer_enable(int32_t max_launches);
+ssd_status ssd_timer_read(ssd_op op, int32_t* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ import torch  # provides the process's HIP runtime, which libssd then shares
 
 __all__ = [
     "SSDError", "softmax_t", "topf", "saguaro_sample", "verify", "cache_keys", "cache_lookup",
-    "fanout", "workspace_bytes", "stats_fields", "LIB_PATH",
+    "fanout", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
@@ -51,6 +51,10 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.ssd_timer_enable.argtypes = [_i32]
+    lib.ssd_timer_enable.restype = ctypes.c_int
+    lib.ssd_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(_i32), ctypes.POINTER(_f64)]
+    lib.ssd_timer_read.restype = ctypes.c_int
     lib.ssd_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i32, _i64]
     lib.ssd_workspace_bytes.restype = _sz
     lib.ssd_status_string.argtypes = [ctypes.c_int]
@@ -113,6 +117,19 @@ def _rows_ld(x, nd):
     return ld
 
 
+def timer_enable(max_launches):
+    """Bracket up to max_launches streaming-pass launches per op with HIP
+    events on their stream (0 disables)."""
+    _check(_lib.ssd_timer_enable(int(max_launches)), "ssd_timer_enable")
+
+
+def timer_read(op):
+    """(launches timed, their total duration in ms) for `op` since enabling."""
+    n, t = _i32(0), _f64(0.0)
+    _check(_lib.ssd_timer_read(op, ctypes.byref(n), ctypes.byref(t)), "ssd_timer_read")
+    return n.value, t.value
+
+
 def workspace_bytes(op, n, K, V):
     return int(_lib.ssd_workspace_bytes(op, n, K, V))
 
@@ -121,8 +138,8 @@ _WS = {}
 
 
 def _workspace(op, n, K, V, dev):
-    """Zero-filled workspace, cached per (op, shape, device) and reused: each
-    call leaves its counters cleared.  Calls sharing one must not overlap."""
+    """Workspace cached per (op, shape, device) and reused (its contents do
+    not matter).  Calls sharing one must not overlap."""
     key = (op, n, K, V, dev)
     w = _WS.get(key)
     if w is None:

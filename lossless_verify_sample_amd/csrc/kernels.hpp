@@ -26,7 +26,7 @@ namespace ssd {
 enum Mode { M_SOFTMAX = 0, M_TOPF = 1, M_SAMPLE = 2, M_VERIFY = 3 };
 
 constexpr int CH = 8;             // blocks per workgroup in the streaming pass (2 per wave)
-constexpr int CH_R = 4;           // blocks per workgroup in the residual pass (1 per wave)
+constexpr int CH_R = 2 * EWG / 64;  // blocks per workgroup in the residual pass (2 per wave)
 constexpr int TPT = BLK / EWG;    // tokens per epilogue thread in a token stage
 constexpr int NBT = MAX_NB / EWG; // blocks per epilogue thread
 constexpr int NBL = MAX_NB / 64;  // blocks per lane when a wave holds a whole row
@@ -92,6 +92,7 @@ struct ESm {
   uint64_t wk[ENW][64];     // each wave's own top-F exchange row
   int nre;                  // candidates appended by block re-reads
   int ks;
+  SeqState ss;
   float vm[MAX_K1];         // verification, per row j <= K
   double vL[MAX_K1];
   int vfb[MAX_K1];
@@ -560,7 +561,7 @@ __device__ __forceinline__ void epi_softmax_p(const Params& p, int64_t row) {
   const double tot = greedy ? 1.0 : wave_sum_d(w);
   if (lane == 0) {
     ssd_row_stats st;
-    st.lse = greedy ? 0.0 : log(tot);
+    st.lse = greedy ? 0.0 : ln_fast(tot);
     st.max = m;
     st.argmax = am < 0 ? 0 : am;  // (a NaN row matches no block)
     p.stats[row] = st;
@@ -625,7 +626,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   // sigma_{F,C}: lane f < F holds 2^((z_f - m) s) of the f-th member of S
   const float es = (!greedy && lane < F) ? __builtin_amdgcn_exp2f((tv - m) * s) : 0.f;
   const double zs = wave_sum_d((double)es);
-  const double lse = greedy ? 0.0 : log((tot0 - zs) + (double)C * zs);
+  const double lse = greedy ? 0.0 : ln_fast((tot0 - zs) + (double)C * zs);
   if (tid < 64) {
     if (lane < p.F_out) {
       if (p.out_idx) p.out_idx[row * p.F_out + lane] = ti;
@@ -684,7 +685,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
 #pragma unroll
     for (int e = 1; e < TPT; ++e) zx = (d == (uint32_t)e) ? z[e] : zx;
     const bool inS = (smask >> d) & 1u;
-    const double lq = ((double)zx - (double)m) * (1.0 / (double)T) + (inS ? log((double)C) : 0.0) - lse;
+    const double lq = ((double)zx - (double)m) * (1.0 / (double)T) + (inS ? ln_fast((double)C) : 0.0) - lse;
     p.tokens[b * p.K + j] = x;
     p.q[b * p.K + j] = __builtin_amdgcn_exp2f((float)(lq * LOG2E));
   } else if (x < 0 && tid == 0) {
@@ -693,8 +694,19 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   }
 }
 
+// Acceptance and residual pass of verification, one workgroup per (sequence,
+// chunk of CH_R blocks).  Every workgroup of a sequence merges the partials
+// of its K + 1 target rows and takes the acceptance decisions itself (the
+// same arithmetic in each, so all agree on k*); this costs a few KB of L2
+// reads per workgroup and saves a kernel boundary and a dependent load.
+// Chunk 0 writes the per-sequence outputs and, when every draft token is
+// accepted or the sequence is greedy, the bonus token.  When T > 0 and k* <
+// K each workgroup adds the residual block sums of its chunk: sums of
+// max(0, p - sigma) over target row k* and draft row k*, in the target's
+// units scaled by exp(L_t) 2^(eps_t) (a constant per sequence), with the
+// target block maxima.
 template <int DT, bool AL, int PLN>
-__device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
+__device__ __forceinline__ void accept_residual(const Params& p, int b, int chunk, ESm& sm) {
   const int K = p.K, K1 = K + 1, NB = p.NB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int V = (int)p.V;
@@ -704,6 +716,7 @@ __device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
   const double invT = greedy ? 0.0 : 1.0 / (double)T;
   const int64_t r0 = (int64_t)b * K1;
   const int64_t rs = p.ld * Dt<DT>::SZ;
+  const bool lead = chunk == 0;
   // wave 0, lane j < K: drafted token, sigma_j(x_j), the target logit at x_j
   // captured by the streaming pass; lane j <= K: the draft row statistics
   int xj = -1;
@@ -738,7 +751,7 @@ __device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
       }
     }
     wsum = wave_sum_d(wsum);
-    if (j == K) {
+    if (lead && j == K) {
 #pragma unroll
       for (int i = 0; i < PLN; ++i) {
         const int be = lane + 64 * i;
@@ -750,8 +763,8 @@ __device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
     }
     if (lane == 0) {
       sm.vm[j] = m;
-      sm.vL[j] = greedy ? 0.0 : log(wsum);
-      sm.vfb[j] = fb < 0 ? 0 : fb;      // (a NaN row matches no block)
+      sm.vL[j] = greedy ? 0.0 : ln_fast(wsum);
+      sm.vfb[j] = fb < 0 ? 0 : fb;                  // (a NaN row matches no block)
       sm.vam[j] = greedy ? (am < 0 ? 0 : am) : -1;  // greedy rows carry the block argmax in their partial
     }
   };
@@ -765,7 +778,7 @@ __device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
   }
   __syncthreads();
   // argmax of the T > 0 rows is only needed for the optional statistics
-  if (!greedy && p.stats) {
+  if (lead && !greedy && p.stats) {
     for (int j = wave; j < K1; j += ENW) {
       const int am = wave_first_eq<DT, AL>(p.x + (r0 + j) * rs, V, sm.vfb[j], sm.vm[j]);
       if (lane == 0) sm.vam[j] = am;
@@ -775,22 +788,20 @@ __device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
   // acceptance decisions (wave 0, lane j < K) and p_j(x_j) for every position
   if (wave == 0) {
     bool acc = false;
-    if (lane < K) {
-      double pj = 0.0;
-      if (xj >= 0 && xj < V) {
-        if (greedy) {
-          acc = (xj == sm.vam[lane]);
-          pj = acc ? 1.0 : 0.0;
-        } else {
-          pj = exp(((double)ztj - (double)sm.vm[lane]) * invT - sm.vL[lane]);
-          const double q = (double)qj;
-          const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
-          const float u = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
-          acc = (double)u < rho;
-        }
+    double pj = 0.0;
+    if (lane < K && xj >= 0 && xj < V) {
+      if (greedy) {
+        acc = (xj == sm.vam[lane]);
+        pj = acc ? 1.0 : 0.0;
+      } else {
+        pj = exp_fast(((double)ztj - (double)sm.vm[lane]) * invT - sm.vL[lane]);
+        const double q = (double)qj;
+        const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
+        const float u = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
+        acc = (double)u < rho;
       }
-      p.p_out[b * K + lane] = (float)pj;
     }
+    if (lead && lane < K) p.p_out[b * K + lane] = (float)pj;
     const uint64_t rej = __ballot(lane < K && !acc);
     const int ks = rej ? (int)__builtin_ctzll(rej) : K;
     SeqState ss{};
@@ -809,17 +820,20 @@ __device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
       const double ed = (double)ss.o_d + (double)md * (double)s;
       ss.invT = invT;
       ss.D0 = ((double)mt - (double)md) * invT + Lt - Ld;
-      ss.lnC = log((double)p.C);
-      ss.kf = (float)(exp2(et - ed) * exp(Lt - Ld));
+      ss.lnC = ln_fast((double)p.C);
+      ss.kf = (float)exp_fast((et - ed) * LN2 + (Lt - Ld));
     }
     if (lane == 0) {
       sm.ks = ks;
-      p.acc_len[b] = ks;
-      p.state[b] = ss;
-      if (greedy) p.bonus[b] = sm.vam[ks];
+      sm.ss = ss;
+      if (lead) {
+        p.acc_len[b] = ks;
+        p.state[b] = ss;
+        if (greedy) p.bonus[b] = sm.vam[ks];
+      }
     }
   }
-  if (p.stats && tid < K1) {
+  if (lead && p.stats && tid < K1) {
     ssd_row_stats st;
     st.lse = sm.vL[tid];
     st.max = sm.vm[tid];
@@ -828,41 +842,106 @@ __device__ __forceinline__ void epi_verify_p(const Params& p, int b, ESm& sm) {
   }
   if (greedy) return;
   __syncthreads();
-  if (sm.ks < K) return;
-  // all K accepted: bonus ~ p_K (row K's partials are in sm.M / sm.S)
-  const float m = sm.vm[K];
-  int beta = block_stage(NB, p.seed, b, K, ST_BONUS_BLOCK, sm.ru[0], [&](int be, int) -> float {
-    return block_w(sm.M[be], sm.S[be], m, s);
-  });
-  if (beta < 0) beta = 0;
-  const unsigned char* rp = p.x + (r0 + K) * rs;
-  const int x0 = beta * BLK + TPT * tid;
-  float z[TPT];
-  load_run<DT, AL>(rp, V, x0, z);
-  const float Mb = sm.M[beta];
-  const int x = token_race(x0, V, p.seed, b, K, ST_BONUS_TOKEN, sm.ru[1], [&](int e) -> float {
-    return z[e] > -INFINITY ? (Mb - z[e]) * s : INFINITY;
-  });
-  if (tid == 0) p.bonus[b] = x >= 0 ? x : 0;
+  const int ks = sm.ks;
+  if (ks == K) {
+    if (!lead) return;
+    // all K accepted: bonus ~ p_K (row K's partials are in sm.M / sm.S)
+    const float m = sm.vm[K];
+    int beta = block_stage(NB, p.seed, b, K, ST_BONUS_BLOCK, sm.ru[0], [&](int be, int) -> float {
+      return block_w(sm.M[be], sm.S[be], m, s);
+    });
+    if (beta < 0) beta = 0;
+    const unsigned char* rp = p.x + (r0 + K) * rs;
+    const int x0 = beta * BLK + TPT * tid;
+    float z[TPT];
+    load_run<DT, AL>(rp, V, x0, z);
+    const float Mb = sm.M[beta];
+    const int x = token_race(x0, V, p.seed, b, K, ST_BONUS_TOKEN, sm.ru[1], [&](int e) -> float {
+      return z[e] > -INFINITY ? (Mb - z[e]) * s : INFINITY;
+    });
+    if (tid == 0) p.bonus[b] = x >= 0 ? x : 0;
+    return;
+  }
+  // residual block sums of this chunk's blocks (two per wave, all loads in flight together)
+  const int be0 = chunk * CH_R + wave, be1 = be0 + ENW;
+  if (be0 >= NB) return;
+  const SeqState ss = sm.ss;
+  const int64_t row = r0 + ks;
+  const unsigned char* rt = p.x + row * rs;
+  const unsigned char* rd = p.xd + row * rs;
+  RawBlock<DT, AL> ut0, ud0, ut1, ud1;
+  if ((chunk + 1) * CH_R * BLK <= V) {
+    load_raw<DT, AL, true>(rt, V, be0, lane, ut0);
+    load_raw<DT, AL, true>(rd, V, be0, lane, ud0);
+    load_raw<DT, AL, true>(rt, V, be1, lane, ut1);
+    load_raw<DT, AL, true>(rd, V, be1, lane, ud1);
+  } else {
+    load_raw<DT, AL, false>(rt, V, be0, lane, ut0);
+    load_raw<DT, AL, false>(rd, V, be0, lane, ud0);
+    load_raw<DT, AL, false>(rt, V, min(be1, NB - 1), lane, ut1);
+    load_raw<DT, AL, false>(rd, V, min(be1, NB - 1), lane, ud1);
+  }
+  const float ot = ss.o_t, od = ss.o_d, nk = -ss.kf;
+  const int64_t rrow = row * p.ld_dtopf;
+  auto residual = [&](const RawBlock<DT, AL>& ut, const RawBlock<DT, AL>& ud, int be) {
+    float vt[32], vd[32];
+    decode_raw<DT, AL>(ut, vt);
+    decode_raw<DT, AL>(ud, vd);
+    float g[32 / Dt<DT>::VW];
+#pragma unroll
+    for (int i = 0; i < 32 / Dt<DT>::VW; ++i) g[i] = group_max<Dt<DT>::VW>(&vt[i * Dt<DT>::VW]);
+    const float Mt = wave_max3(lane_max<32 / Dt<DT>::VW>(g));
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; k += 2) {
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(vt[k], s, ot));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(vd[k], s, od));
+      const float f1 = __builtin_amdgcn_exp2f(fmaf(vt[k + 1], s, ot));
+      const float f2 = __builtin_amdgcn_exp2f(fmaf(vd[k + 1], s, od));
+      a0 += fmaxf(fmaf(nk, e2, e1), 0.f);
+      a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
+    }
+    float R = wave_sum(a0 + a1);
+    // members of the draft's top-F set in this block carry the factor C
+    for (int f = 0; f < p.F; ++f) {
+      const int x = p.dtopf[rrow + f];
+      if (x >= 0 && x < V && x / BLK == be) {
+        const float zt = load_elem<DT>(rt, x), zd = load_elem<DT>(rd, x);
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(zt, s, ot));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(zd, s, od));
+        R += fmaxf(fmaf(nk * p.C, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
+      }
+    }
+    if (lane == 0) p.rpart[(int64_t)b * NB + be] = make_float2(fmaxf(R, 0.f), Mt);
+  };
+  residual(ut0, ud0, be0);
+  if (be1 < NB) residual(ut1, ud1, be1);
 }
 
 template <int DT, bool AL>
 __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqState& ss, ESm& sm) {
-  const int tid = threadIdx.x, K1 = p.K + 1, NB = p.NB, ks = ss.kstar, V = (int)p.V, F = p.F;
+  const int tid = threadIdx.x, K1 = p.K + 1, NB = p.NB, V = (int)p.V, F = p.F;
+  // the residual sums are read before the hand-over state is known (they are
+  // only used when it asks for them), so both loads are in flight together
+  float R[NBT], Mt[NBT];
+#pragma unroll
+  for (int k = 0; k < NBT; ++k) {
+    const int be = tid + k * EWG;
+    const float2 v = be < NB ? p.rpart[(int64_t)b * NB + be] : make_float2(0.f, -INFINITY);
+    R[k] = v.x;
+    Mt[k] = v.y;
+  }
+  if (!ss.need) return;
+  const int ks = ss.kstar;
   const int64_t row = (int64_t)b * K1 + ks;
   const int64_t rs = p.ld * Dt<DT>::SZ;
   const unsigned char* rt = p.x + row * rs;
   const unsigned char* rd = p.xd + row * rs;
   const float s = ss.s, mt = ss.m_t;
   // residual block sums with the target row's block maxima
-  float R[NBT];
 #pragma unroll
-  for (int k = 0; k < NBT; ++k) {
-    const int be = tid + k * EWG;
-    const float2 v = be < NB ? p.rpart[(int64_t)b * NB + be] : make_float2(0.f, -INFINITY);
-    R[k] = v.x;
-    if (be < NB) sm.M[be] = v.y;
-  }
+  for (int k = 0; k < NBT; ++k)
+    if (tid + k * EWG < NB) sm.M[tid + k * EWG] = Mt[k];
   const int any = __syncthreads_or(R[0] > 0.f || R[1] > 0.f);
   float M[NBT], S[NBT];
   if (!any) {  // no residual mass: p_k* from the target row's partials
@@ -961,66 +1040,18 @@ __global__ __launch_bounds__(EWG) void k_epi(Params p) {
   const int g = blockIdx.x;
   // rows of up to 128 blocks (V <= 262144) keep two partials per lane
   const bool small = p.NB <= 128;
-  if constexpr (MODE == M_VERIFY) small ? epi_verify_p<DT, AL, 2>(p, g, sm) : epi_verify_p<DT, AL, NBL>(p, g, sm);
   if constexpr (MODE == M_SOFTMAX) small ? epi_softmax_p<DT, AL, 2>(p, g) : epi_softmax_p<DT, AL, NBL>(p, g);
   if constexpr (MODE == M_TOPF) small ? epi_topf_p<DT, AL, 2>(p, g, sm) : epi_topf_p<DT, AL, NBL>(p, g, sm);
   if constexpr (MODE == M_SAMPLE) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
 }
 
-// Residual pass for sequences rejected at k* < K: block sums of
-// max(0, p - sigma) over target row k* and draft row k*, in the target's
-// units scaled by exp(L_t) 2^(eps_t) (a constant per sequence).  One block
-// per wave; no LDS and no barrier.
+// Acceptance and residual pass (one workgroup per sequence and chunk).
 template <int DT, bool AL>
-__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 5) void k_residual(Params p) {
-  const int item = blockIdx.x;
-  const int b = item / p.nchunk;
-  const int chunk = item - b * p.nchunk;
-  const SeqState ss = p.state[b];
-  if (!ss.need) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K1 = p.K + 1, V = (int)p.V;
-  const int64_t row = (int64_t)b * K1 + ss.kstar;
-  const int64_t rs = p.ld * Dt<DT>::SZ;
-  const unsigned char* rt = p.x + row * rs;
-  const unsigned char* rd = p.xd + row * rs;
-  const int be = chunk * CH_R + wave;
-  if (be >= p.NB) return;
-  float vt[32], vd[32];
-  if ((be + 1) * BLK <= V) {
-    load_block_full<DT, AL>(rt, be, lane, vt);
-    load_block_full<DT, AL>(rd, be, lane, vd);
-  } else {
-    load_block<DT, AL>(rt, V, be, lane, vt);
-    load_block<DT, AL>(rd, V, be, lane, vd);
-  }
-  const float s = ss.s, ot = ss.o_t, od = ss.o_d, nk = -ss.kf;
-  float g[32 / Dt<DT>::VW];
-#pragma unroll
-  for (int i = 0; i < 32 / Dt<DT>::VW; ++i) g[i] = group_max<Dt<DT>::VW>(&vt[i * Dt<DT>::VW]);
-  const float Mt = wave_max3(lane_max<32 / Dt<DT>::VW>(g));
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-  for (int k = 0; k < 32; k += 2) {
-    const float e1 = __builtin_amdgcn_exp2f(fmaf(vt[k], s, ot));
-    const float e2 = __builtin_amdgcn_exp2f(fmaf(vd[k], s, od));
-    const float f1 = __builtin_amdgcn_exp2f(fmaf(vt[k + 1], s, ot));
-    const float f2 = __builtin_amdgcn_exp2f(fmaf(vd[k + 1], s, od));
-    a0 += fmaxf(fmaf(nk, e2, e1), 0.f);
-    a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
-  }
-  float R = wave_sum(a0 + a1);
-  // members of the draft's top-F set in this block carry the factor C
-  for (int f = 0; f < p.F; ++f) {
-    const int x = p.dtopf[row * p.ld_dtopf + f];
-    if (x >= 0 && x < V && x / BLK == be) {
-      const float zt = load_elem<DT>(rt, x), zd = load_elem<DT>(rd, x);
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(zt, s, ot));
-      const float e2 = __builtin_amdgcn_exp2f(fmaf(zd, s, od));
-      R += fmaxf(fmaf(nk * p.C, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
-    }
-  }
-  if (lane == 0) p.rpart[(int64_t)b * p.NB + be] = make_float2(fmaxf(R, 0.f), Mt);
+__global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(Params p) {
+  __shared__ ESm sm;
+  const int b = blockIdx.x / p.nchunk, chunk = blockIdx.x - b * p.nchunk;
+  if (p.NB <= 128) accept_residual<DT, AL, 2>(p, b, chunk, sm);
+  else accept_residual<DT, AL, NBL>(p, b, chunk, sm);
 }
 
 template <int DT, bool AL>
@@ -1028,7 +1059,6 @@ __global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
   __shared__ ESm sm;
   const int b = blockIdx.x;
   const SeqState ss = p.state[b];
-  if (!ss.need) return;
   epi_residual<DT, AL>(p, b, ss, sm);
 }
 

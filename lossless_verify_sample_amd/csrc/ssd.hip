@@ -5,6 +5,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
+#include <hip/hip_ext.h>
+
 #include "kernels.hpp"
 
 using namespace ssd;
@@ -56,13 +60,20 @@ hipError_t dispatch(int dt, bool al, A... a) {
   return al ? L<SSD_F16, true>::go(a...) : L<SSD_F16, false>::go(a...);
 }
 
-#define SSD_LAUNCHER_T(NAME, KERNEL, THREADS)                                         \
-  template <int DT, bool AL>                                                         \
-  struct NAME {                                                                      \
-    static hipError_t go(int64_t grid, const Params& p, hipStream_t st) {            \
-      KERNEL<<<dim3((unsigned)grid), dim3(THREADS), 0, st>>>(p);                     \
-      return hipGetLastError();                                                      \
-    }                                                                                \
+// Launch on `st`; with timer events the launch itself records them (the
+// HIP extension launch stamps the dispatch, adding no packets of its own).
+#define SSD_LAUNCHER_T(NAME, KERNEL, THREADS)                                              \
+  template <int DT, bool AL>                                                              \
+  struct NAME {                                                                           \
+    static hipError_t go(int64_t grid, const Params& p, hipStream_t st, hipEvent_t e0 = nullptr, \
+                         hipEvent_t e1 = nullptr) {                                       \
+      if (e0) {                                                                           \
+        hipExtLaunchKernelGGL(KERNEL, dim3((unsigned)grid), dim3(THREADS), 0, st, e0, e1, 0, p); \
+      } else {                                                                            \
+        KERNEL<<<dim3((unsigned)grid), dim3(THREADS), 0, st>>>(p);                        \
+      }                                                                                   \
+      return hipGetLastError();                                                           \
+    }                                                                                     \
   };
 #define SSD_LAUNCHER(NAME, KERNEL) SSD_LAUNCHER_T(NAME, KERNEL, WG)
 #define SSD_LAUNCHER_E(NAME, KERNEL) SSD_LAUNCHER_T(NAME, KERNEL, EWG)
@@ -74,8 +85,7 @@ SSD_LAUNCHER(LVerify, (k_stream<DT, AL, M_VERIFY>))
 SSD_LAUNCHER_E(LSoftmaxEpi, (k_epi<DT, AL, M_SOFTMAX>))
 SSD_LAUNCHER_E(LTopfEpi, (k_epi<DT, AL, M_TOPF>))
 SSD_LAUNCHER_E(LSampleEpi, (k_epi<DT, AL, M_SAMPLE>))
-SSD_LAUNCHER_E(LVerifyEpi, (k_epi<DT, AL, M_VERIFY>))
-SSD_LAUNCHER(LResidual, (k_residual<DT, AL>))
+SSD_LAUNCHER_E(LAccept, (k_accept<DT, AL>))
 SSD_LAUNCHER_E(LResidualEpi, (k_residual_epi<DT, AL>))
 SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
 
@@ -86,6 +96,36 @@ bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
 }
 
 const int64_t kMaxGrid = 0x7fffffff;
+
+// Kernel timer: event pairs around the streaming-pass launches, per op.
+struct Timer {
+  int cap = 0;
+  int n[4] = {0, 0, 0, 0};
+  std::vector<hipEvent_t> ev[4];
+};
+Timer g_timer;
+
+void timer_free() {
+  for (auto& v : g_timer.ev) {
+    for (hipEvent_t e : v) (void)hipEventDestroy(e);
+    v.clear();
+  }
+  g_timer.cap = 0;
+  for (int& c : g_timer.n) c = 0;
+}
+
+// The streaming pass of `op`: launch(e0, e1) with the timer's next event
+// pair when it is enabled and has room, else with none.
+template <class F>
+hipError_t timed(ssd_op op, F launch) {
+  if (g_timer.cap > 0 && g_timer.n[op] < g_timer.cap) {
+    const int i = g_timer.n[op];
+    const hipError_t e = launch(g_timer.ev[op][2 * i], g_timer.ev[op][2 * i + 1]);
+    if (e == hipSuccess) ++g_timer.n[op];
+    return e;
+  }
+  return launch(nullptr, nullptr);
+}
 
 }  // namespace
 
@@ -128,7 +168,9 @@ ssd_status ssd_softmax_t(const void* logits, ssd_dtype dt, int64_t rows, int64_t
   const bool al = aligned16(logits, ld, V, dt);
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
-  hipError_t e = dispatch<LSoftmax>(dt, al, rows * nch, p, st);
+  hipError_t e = timed(SSD_OP_SOFTMAX_T, [&](hipEvent_t e0, hipEvent_t e1) {
+    return dispatch<LSoftmax>(dt, al, rows * nch, p, st, e0, e1);
+  });
   if (e == hipSuccess) e = dispatch<LSoftmaxEpi>(dt, al, rows, p, st);
   if (e == hipSuccess && out_probs) {
     p.nchunk = (int)cdiv(NB, NWAVE);
@@ -157,8 +199,11 @@ ssd_status ssd_topf(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, i
   p.out_val = out_val;
   const bool al = aligned16(logits, ld, V, dt);
   (void)hipGetLastError();
-  hipError_t e = dispatch<LTopf>(dt, al, rows * nch, p, (hipStream_t)stream);
-  if (e == hipSuccess) e = dispatch<LTopfEpi>(dt, al, rows, p, (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(SSD_OP_TOPF, [&](hipEvent_t e0, hipEvent_t e1) {
+    return dispatch<LTopf>(dt, al, rows * nch, p, st, e0, e1);
+  });
+  if (e == hipSuccess) e = dispatch<LTopfEpi>(dt, al, rows, p, st);
   return hip_status(e);
 }
 
@@ -195,8 +240,11 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
   p.q = out_q;
   const bool al = aligned16(draft_logits, ld, V, dt);
   (void)hipGetLastError();
-  hipError_t e = dispatch<LSample>(dt, al, rows * nch, p, (hipStream_t)stream);
-  if (e == hipSuccess) e = dispatch<LSampleEpi>(dt, al, rows, p, (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
+    return dispatch<LSample>(dt, al, rows * nch, p, st, e0, e1);
+  });
+  if (e == hipSuccess) e = dispatch<LSampleEpi>(dt, al, rows, p, st);
   return hip_status(e);
 }
 
@@ -243,10 +291,11 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   const bool al = aligned16(target_logits, ld, V, dt) && aligned16(draft_logits, ld, V, dt);
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
-  hipError_t e = dispatch<LVerify>(dt, al, rows * nch, p, st);
-  if (e == hipSuccess) e = dispatch<LVerifyEpi>(dt, al, B, p, st);
+  hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
+    return dispatch<LVerify>(dt, al, rows * nch, p, st, e0, e1);
+  });
   p.nchunk = (int)nchr;
-  if (e == hipSuccess) e = dispatch<LResidual>(dt, al, (int64_t)B * nchr, p, st);
+  if (e == hipSuccess) e = dispatch<LAccept>(dt, al, (int64_t)B * nchr, p, st);
   if (e == hipSuccess) e = dispatch<LResidualEpi>(dt, al, B, p, st);
   return hip_status(e);
 }
@@ -276,6 +325,39 @@ ssd_status ssd_cache_keys(const int32_t* topf_idx, int32_t ld_topf, const int32_
   k_cache_keys<<<dim3((unsigned)cdiv(n, WG)), dim3(WG), 0, (hipStream_t)stream>>>(topf_idx, ld_topf, depth_off,
                                                                                   B, K, Bgt, out_keys);
   return hip_status(hipGetLastError());
+}
+
+ssd_status ssd_timer_enable(int32_t max_launches) {
+  if (max_launches < 0 || max_launches > (1 << 20)) return SSD_ERR_INVALID_ARG;
+  timer_free();
+  if (max_launches == 0) return SSD_OK;
+  for (auto& v : g_timer.ev) {
+    v.resize(2 * (size_t)max_launches);
+    for (hipEvent_t& e : v) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        e = nullptr;
+        timer_free();
+        return SSD_ERR_HIP;
+      }
+    }
+  }
+  g_timer.cap = max_launches;
+  return SSD_OK;
+}
+
+ssd_status ssd_timer_read(ssd_op op, int32_t* launches, double* total_ms) {
+  if (op < SSD_OP_SOFTMAX_T || op > SSD_OP_VERIFY || !launches || !total_ms) return SSD_ERR_INVALID_ARG;
+  double t = 0.0;
+  for (int i = 0; i < g_timer.n[op]; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timer.ev[op][2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.ev[op][2 * i], g_timer.ev[op][2 * i + 1]) != hipSuccess)
+      return SSD_ERR_HIP;
+    t += ms;
+  }
+  *launches = g_timer.n[op];
+  *total_ms = t;
+  return SSD_OK;
 }
 
 ssd_status ssd_fanout(int32_t Bgt, int32_t K, double ratio, int64_t V, int32_t* out_F) {
