@@ -1093,23 +1093,30 @@ __global__ __launch_bounds__(WG) void k_probs(Params p) {
   }
 }
 
-// One wave per sequence: find bonus among depth k*'s keys (lowest slot).
+// One wave per sequence: find the bonus among depth k*'s keys (lowest slot).
+// The depth offsets go through LDS and the sequence's first 64 keys are read
+// together with the accepted length and the bonus, so only the payload gather
+// waits on the decision.
 __global__ __launch_bounds__(WG) void k_lookup(const int32_t* keys, const int32_t* off, const int32_t* payload,
                                                int B, int K, int Bgt, const int32_t* acc, const int32_t* bonus,
                                                int32_t* hit, int32_t* slot, int32_t* toks) {
+  __shared__ int so[MAX_K1 + 1];
+  if ((int)threadIdx.x <= K + 1) so[threadIdx.x] = off[threadIdx.x];
   const int b = blockIdx.x * NWAVE + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (b >= B) return;
-  const int k = acc[b], y = bonus[b];
+  const bool live = b < B;
+  const int k = live ? acc[b] : -1, y = live ? bonus[b] : 0;
+  const int key0 = (live && lane < Bgt) ? keys[(int64_t)b * Bgt + lane] : 0;
+  __syncthreads();
+  if (!live) return;
   int found = -1;
   if (k >= 0 && k <= K) {
-    int lo = off[k], hi = off[k + 1];
-    lo = max(lo, 0);
-    hi = min(hi, Bgt);
+    const int lo = max(so[k], 0), hi = min(so[k + 1], Bgt);
     for (int s0 = lo; s0 < hi; s0 += 64) {
       const int sl = s0 + lane;
-      const bool mt = sl < hi && keys[(int64_t)b * Bgt + sl] == y;
-      const uint64_t m = __ballot(mt);
+      const int sh = __shfl(key0, sl & 63);  // every lane takes part in the shuffle
+      const int kv = sl < 64 ? sh : keys[(int64_t)b * Bgt + min(sl, Bgt - 1)];
+      const uint64_t m = __ballot(sl < hi && kv == y);
       if (m) {
         found = s0 + __builtin_ctzll(m);
         break;
@@ -1124,21 +1131,24 @@ __global__ __launch_bounds__(WG) void k_lookup(const int32_t* keys, const int32_
     toks[(int64_t)b * K + i] = found >= 0 ? payload[((int64_t)b * Bgt + found) * K + i] : -1;
 }
 
+// Keys of every (sequence, slot): slot sl of depth k (off[k] <= sl < off[k+1])
+// holds entry sl - off[k] of that depth's top list.  The depth offsets go
+// through LDS.
 __global__ __launch_bounds__(WG) void k_cache_keys(const int32_t* topf, int ldf, const int32_t* off, int B, int K,
                                                    int Bgt, int32_t* keys) {
+  __shared__ int so[MAX_K1 + 1];
+  if ((int)threadIdx.x <= K + 1) so[threadIdx.x] = off[threadIdx.x];
+  __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * WG + threadIdx.x;
   if (t >= (int64_t)B * Bgt) return;
   const int b = (int)(t / Bgt), sl = (int)(t - (int64_t)b * Bgt);
-  int val = -1;
-  for (int k = 0; k <= K; ++k) {
-    const int lo = off[k], hi = off[k + 1];
-    if (sl >= lo && sl < hi) {
-      const int i = sl - lo;
-      if (i < ldf) val = topf[((int64_t)b * (K + 1) + k) * ldf + i];
-      break;
+  int kk = -1, i = 0;
+  for (int k = K; k >= 0; --k)  // descending: the first depth whose range holds sl wins
+    if (sl >= so[k] && sl < so[k + 1]) {
+      kk = k;
+      i = sl - so[k];
     }
-  }
-  keys[t] = val;
+  keys[t] = (kk >= 0 && i < ldf) ? topf[((int64_t)b * (K + 1) + kk) * ldf + i] : -1;
 }
 
 }  // namespace ssd
