@@ -2,9 +2,10 @@
 """Benchmark of the batched lossless verify-and-resample step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic logits:
-draft sampling with Saguaro sigma_{F,C} (ssd_saguaro_sample), verification
-(ssd_verify: acceptance, accepted prefix, bonus), speculation-cache key build
-and lookup (ssd_cache_keys, ssd_cache_lookup).  Default workload: B=64, K=7,
+draft sampling with Saguaro sigma_{F,C} (ssd_saguaro_sample, which also
+writes the speculation-cache keys: each draft row's top-F_k list under the
+truncated-geometric fan-out), verification (ssd_verify: acceptance, accepted
+prefix, bonus, and the cache lookup of (k*, bonus)).  Default workload: B=64, K=7,
 V=151936 (Qwen-3 vocabulary), bf16 logits, T=1, F=4, C=0.5; cache budget 64
 with fan-out ratio 0.6.  Inputs rotate over > 1 GiB of distinct sets so the
 256 MB Infinity Cache cannot serve them.  Prints one JSON line.
@@ -121,18 +122,15 @@ def main():
     sets = [W.logits(cfg, i, dev) for i in range(nsets)]
     T = W.temperatures(cfg, dev)
     use_cache = not a.no_cache
+    Fo = cfg.fout
     if use_cache:
         Fk = ssd.fanout(a.cache_budget, K, a.cache_ratio, V)
-        Fo = max(cfg.fout, max(Fk))
-        off_h = [0]
-        for f in Fk:
-            off_h.append(off_h[-1] + f)
-        off = torch.tensor(off_h, dtype=torch.int32, device=dev)
-        payloads = [W.payload(cfg, a.cache_budget, i, dev) for i in range(nsets)]
+        caches = [ssd.Cache(Fk, B, K, dev, payload=W.payload(cfg, a.cache_budget, i, dev)) for i in range(nsets)]
     else:
-        Fk, Fo = None, cfg.fout
+        Fk, caches = None, None
     total = a.warmup + a.steps
     acc_buf = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    hit_buf = torch.zeros((total, B), dtype=torch.int32, device=dev)
     smp_out = dict(tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
                    q=torch.empty((B, K), dtype=torch.float32, device=dev),
                    stats=torch.empty((cfg.rows, 2), dtype=torch.float64, device=dev),
@@ -141,7 +139,6 @@ def main():
     bonus = torch.empty(B, dtype=torch.int32, device=dev)
     pout = torch.empty((B, K), dtype=torch.float32, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
-    hit_list = []
 
     def step(i, instrument=False):
         t, d = sets[i % nsets]
@@ -149,19 +146,17 @@ def main():
         e = ev[i] if instrument else None
         if e:
             e[0].record()
-        ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=Fo, out=smp_out)
+        cache = caches[i % nsets] if use_cache else None
+        if cache is not None:
+            cache.hit = hit_buf[i]
+        ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=Fo, out=smp_out, cache=cache)
         if e:
             e[1].record()
         ver_out = dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None)
         ssd.verify(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["q"], smp_out["stats"],
-                   smp_out["topf_idx"], out=ver_out)
+                   smp_out["topf_idx"], out=ver_out, cache=cache)
         if e:
             e[2].record()
-        if use_cache:
-            keys = ssd.cache_keys(smp_out["topf_idx"], off, a.cache_budget)
-            h, _, _ = ssd.cache_lookup(keys, off, payloads[i % nsets], acc_buf[i], bonus)
-            if not instrument and i >= a.warmup:
-                hit_list.append(h)
         if e:
             e[3].record()
 
@@ -233,7 +228,7 @@ def main():
         "ms_cache": round(t_c, 5),
         "gbs_sample": round(gbs_sample, 1),
         "gbs_verify": round(gbs_verify, 1),
-        "cache_hit_rate": round(float(torch.stack(hit_list).sum().item()) / (a.steps * B), 4) if use_cache else None,
+        "cache_hit_rate": round(float(hit_buf[a.warmup:].sum().item()) / (a.steps * B), 4) if use_cache else None,
         "roofline": {
             "kernel": kname,
             "bound": "hbm",

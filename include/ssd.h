@@ -97,6 +97,31 @@ typedef struct {
   int32_t argmax;
 } ssd_row_stats;
 
+/* Speculation-cache descriptor shared by sampling and verification ([SSD-B]
+ * core-mechanism section: the draft prepares K-token continuations keyed by
+ * the possible verification outcomes (accepted length k, bonus token) while
+ * the target verifies, and one lookup follows; part 1: F_k guesses at depth
+ * k under the budget Bgt = sum F_k).  A host struct; `fanout` is host memory,
+ * the other arrays device memory owned by the caller.
+ *   fanout     host int32 [K+1]: F_k >= 0, each <= min(SSD_MAX_F, V)
+ *              (e.g. from ssd_fanout); slots are depth-major, depth k at
+ *              [off_k, off_k + F_k) with off_k = F_0 + ... + F_{k-1}
+ *   keys       device int32 [B, Bgt]: ssd_saguaro_sample writes, for each
+ *              row j, its top-F_j draft tokens (value desc, index asc) at
+ *              depth j; ssd_verify reads them
+ *   payload    device int32 [B, Bgt, K]: the K pre-speculated tokens of a slot
+ *              (ssd_verify; may be NULL when K = 0)
+ *   out_hit, out_slot  device int32 [B]; out_tokens device int32 [B, K]
+ *              (ssd_verify): as ssd_cache_lookup. */
+typedef struct {
+  const int32_t* fanout;
+  int32_t* keys;
+  const int32_t* payload;
+  int32_t* out_hit;
+  int32_t* out_slot;
+  int32_t* out_tokens;
+} ssd_cache;
+
 /* Temperature softmax row statistics ([SSD-A] and [SSD-B] part 2 name the
  * sampling temperature; p = softmax(z / T)).
  *   logits      device [rows, ld] of dtype dt, V <= ld
@@ -136,13 +161,18 @@ ssd_status ssd_topf(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, i
  *   out_stats    ssd_row_stats [B, K+1]: lse = ln sum w relative to max
  *   out_topf_idx int32 [B, K+1, F_out] or NULL when F_out = 0
  *   out_topf_val float [B, K+1, F_out] or NULL
+ *   cache        NULL, or a cache descriptor whose `keys` receive each row j's
+ *                top-F_j list (only fanout and keys are used here); row j then
+ *                ranks max(F, F_out, F_j) entries
  * Row K is not sampled; its stats and top-F predict the bonus after K
- * acceptances.  workspace: ssd_workspace_bytes(SSD_OP_SAMPLE, B, K, V). */
+ * acceptances.  workspace: ssd_workspace_bytes(SSD_OP_SAMPLE, B, K, V).
+ * Errors: also a fan-out entry < 0 or > min(SSD_MAX_F, V), or cache without
+ * keys. */
 ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K, int64_t V,
                               int64_t ld, const float* temperature, int32_t F, float C, int32_t F_out,
                               uint64_t seed, int32_t* out_tokens, float* out_q, ssd_row_stats* out_stats,
-                              int32_t* out_topf_idx, float* out_topf_val, void* workspace,
-                              size_t ws_bytes, void* stream);
+                              int32_t* out_topf_idx, float* out_topf_val, const ssd_cache* cache,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /* Target side: lossless acceptance test, accepted prefix and bonus token
  * ([SSD-A]: the target accepts a prefix of the drafted tokens and samples one
@@ -169,13 +199,18 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
  * Outputs (device): out_accept_len int32 [B]; out_bonus int32 [B];
  *   out_p float [B, K] = p_j(x_j) for every j; out_target_stats
  *   ssd_row_stats [B, K+1] or NULL.
- * workspace: ssd_workspace_bytes(SSD_OP_VERIFY, B, K, V). */
+ *   cache  NULL, or a cache descriptor: the realised (k*, bonus) is looked up
+ *          among depth k*'s keys as ssd_cache_lookup does, in the same
+ *          kernel that draws the bonus.
+ * workspace: ssd_workspace_bytes(SSD_OP_VERIFY, B, K, V).
+ * Errors: also a bad fan-out (as for sampling) or a cache missing keys,
+ * outputs, or the payload when K > 0 and Bgt > 0. */
 ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K,
                       int64_t V, int64_t ld, const float* temperature, int32_t F, float C, uint64_t seed,
                       const int32_t* draft_tokens, const float* draft_q, const ssd_row_stats* draft_stats,
                       const int32_t* draft_topf_idx, int32_t ld_topf, int32_t* out_accept_len,
-                      int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, void* workspace,
-                      size_t ws_bytes, void* stream);
+                      int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, const ssd_cache* cache,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 /* Speculation-cache lookup keyed by (accepted length, bonus token) ([SSD-B]
  * core-mechanism section: the draft builds a speculation cache while the

@@ -14,7 +14,7 @@ import os
 import torch  # provides the process's HIP runtime, which libssd then shares
 
 __all__ = [
-    "SSDError", "softmax_t", "topf", "saguaro_sample", "verify", "cache_keys", "cache_lookup",
+    "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "cache_keys", "cache_lookup",
     "fanout", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
 ]
 
@@ -32,6 +32,52 @@ class SSDError(RuntimeError):
     pass
 
 
+class _CacheStruct(ctypes.Structure):
+    _fields_ = [("fanout", _vp), ("keys", _vp), ("payload", _vp), ("out_hit", _vp), ("out_slot", _vp),
+                ("out_tokens", _vp)]
+
+
+class Cache:
+    """Speculation-cache descriptor (ssd_cache): the per-depth fan-out (host
+    ints, e.g. from fanout()), the depth-major keys [B, Bgt] that sampling
+    writes, and for verification the payload [B, Bgt, K] and the lookup
+    outputs hit [B], slot [B], tokens [B, K] (allocated when not given)."""
+
+    def __init__(self, fanout, B, K, device, payload=None, keys=None, hit=None, slot=None, tokens=None):
+        self.fanout = [int(f) for f in fanout]
+        if len(self.fanout) != K + 1:
+            raise SSDError("fanout must have K+1 entries")
+        self.Bgt = sum(self.fanout)
+        self.B, self.K = B, K
+        self._fan = (ctypes.c_int32 * (K + 1))(*self.fanout)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.keys = keys if keys is not None else torch.empty((B, self.Bgt), **i32)
+        self.payload = payload
+        self.hit = hit if hit is not None else torch.empty(B, **i32)
+        self.slot = slot if slot is not None else torch.empty(B, **i32)
+        self.tokens = tokens if tokens is not None else torch.empty((B, K), **i32)
+        off = [0]
+        for f in self.fanout:
+            off.append(off[-1] + f)
+        self.depth_off = torch.tensor(off, **i32)
+
+    def _struct(self, dev, verify):
+        _need(self.keys, torch.int32, "cache keys", dev)
+        if tuple(self.keys.shape) != (self.B, self.Bgt):
+            raise SSDError("cache keys must be [B, Bgt]")
+        st = _CacheStruct(ctypes.cast(self._fan, _vp), _p(self.keys))
+        if verify:
+            if self.K > 0 and self.Bgt > 0:
+                _need(self.payload, torch.int32, "cache payload", dev)
+                if tuple(self.payload.shape) != (self.B, self.Bgt, self.K):
+                    raise SSDError("cache payload must be [B, Bgt, K]")
+                st.payload = _p(self.payload)
+            for t, n in ((self.hit, "hit"), (self.slot, "slot"), (self.tokens, "tokens")):
+                _need(t, torch.int32, "cache " + n, dev)
+            st.out_hit, st.out_slot, st.out_tokens = _p(self.hit), _p(self.slot), _p(self.tokens)
+        return st
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m lossless_verify_sample_amd.build`")
@@ -40,9 +86,9 @@ def _load():
         "ssd_softmax_t": [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp],
         "ssd_topf": [_vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp],
         "ssd_saguaro_sample": [_vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _i32, _u64, _vp, _vp, _vp,
-                               _vp, _vp, _vp, _sz, _vp],
+                               _vp, _vp, _vp, _vp, _sz, _vp],
         "ssd_verify": [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _u64, _vp, _vp, _vp, _vp, _i32,
-                       _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                       _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
         "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
@@ -192,12 +238,13 @@ def topf(logits, F):
     return idx, val
 
 
-def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None):
+def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=None):
     """Draft sampling with sigma_{F,C} over draft logits [B, K+1, V].
 
     Returns dict(tokens [B,K] int32, q [B,K] f32, stats [B*(K+1), 2] (see
     stats_fields), topf_idx [B,K+1,F_out] int32, topf_val [B,K+1,F_out] f32).
-    `out` may pass a dict of preallocated outputs with those keys."""
+    `out` may pass a dict of preallocated outputs with those keys.  With a
+    Cache, row j also writes its top-F_j tokens into cache.keys."""
     ld = _rows_ld(draft, 3)
     B, K1, V = draft.shape
     K = K1 - 1
@@ -215,17 +262,20 @@ def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None):
     ws = _workspace(OP_SAMPLE, B, K, V, dev)
     _check(_lib.ssd_saguaro_sample(_p(draft), _DT[draft.dtype], B, K, V, ld, _p(temperature), F, float(C), F_out,
                                    int(seed) & (2 ** 64 - 1), _p(out["tokens"]), _p(out["q"]), _p(out["stats"]),
-                                   _p(out["topf_idx"]), _p(out["topf_val"]), _p(ws), ws.numel(), _stream(dev)),
+                                   _p(out["topf_idx"]), _p(out["topf_val"]),
+                                   ctypes.byref(cache._struct(dev, False)) if cache is not None else None,
+                                   _p(ws), ws.numel(), _stream(dev)),
            "ssd_saguaro_sample")
     return out
 
 
 def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats, draft_topf_idx, want_stats=False,
-           out=None):
+           out=None, cache=None):
     """Acceptance test, accepted length and bonus for target/draft [B, K+1, V].
 
     Returns dict(accept_len [B] int32, bonus [B] int32, p [B,K] f32, stats
-    [B*(K+1), 2] or None)."""
+    [B*(K+1), 2] or None).  With a Cache, (k*, bonus) is also looked up and
+    cache.hit / cache.slot / cache.tokens are written."""
     ld = _rows_ld(target, 3)
     if draft.shape != target.shape or draft.dtype != target.dtype or _rows_ld(draft, 3) != ld:
         raise SSDError("target and draft logits must share shape, dtype and row stride")
@@ -249,7 +299,9 @@ def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats,
     _check(_lib.ssd_verify(_p(target), _p(draft), _DT[target.dtype], B, K, V, ld, _p(temperature), F, float(C),
                            int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_q), _p(draft_stats),
                            _p(draft_topf_idx) if F > 0 else None, ldf, _p(out["accept_len"]), _p(out["bonus"]),
-                           _p(out["p"]), _p(out.get("stats")), _p(ws), ws.numel(), _stream(dev)), "ssd_verify")
+                           _p(out["p"]), _p(out.get("stats")),
+                           ctypes.byref(cache._struct(dev, True)) if cache is not None else None,
+                           _p(ws), ws.numel(), _stream(dev)), "ssd_verify")
     return out
 
 

@@ -76,6 +76,15 @@ struct Params {
   float* p_out;
   SeqState* state;
   float2* rpart;            // residual block sums and target block maxima [B, NB]
+  // speculation cache (optional): depth offsets, keys, payload, lookup outputs
+  int koff[MAX_K1 + 1];
+  int Bgt;
+  int lookup;               // verification looks (k*, bonus) up
+  int32_t* ckeys;           // [B, Bgt]; sampling writes, verification reads
+  const int32_t* cpay;      // [B, Bgt, K]
+  int32_t* chit;
+  int32_t* cslot;
+  int32_t* ctok;
 };
 
 // LDS of an epilogue workgroup.
@@ -92,6 +101,7 @@ struct ESm {
   uint64_t wk[ENW][64];     // each wave's own top-F exchange row
   int nre;                  // candidates appended by block re-reads
   int ks;
+  int bonus;
   SeqState ss;
   float vm[MAX_K1];         // verification, per row j <= K
   double vL[MAX_K1];
@@ -620,7 +630,9 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
     ws += (double)w[i];
   }
   const double tot0 = greedy ? 1.0 : wave_sum_d(ws);
-  const uint64_t tkey = wave_topf<DT, AL, PLN>(rp, V, NB, p.F_sel, r, m, sm);
+  // entries ranked: F for sigma, F_out listed, and this depth's cache keys
+  const int Fj = p.ckeys ? p.koff[j + 1] - p.koff[j] : 0;
+  const uint64_t tkey = wave_topf<DT, AL, PLN>(rp, V, NB, max(p.F_sel, Fj), r, m, sm);
   const float tv = key_val(tkey);
   const int ti = (int)key_idx(tkey);
   // sigma_{F,C}: lane f < F holds 2^((z_f - m) s) of the f-th member of S
@@ -632,6 +644,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
       if (p.out_idx) p.out_idx[row * p.F_out + lane] = ti;
       if (p.out_val) p.out_val[row * p.F_out + lane] = tv;
     }
+    if (lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = ti;
     if (lane == 0) {
       ssd_row_stats st;
       st.lse = lse;
@@ -919,19 +932,9 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
 }
 
 template <int DT, bool AL>
-__device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqState& ss, ESm& sm) {
+__device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqState& ss, const float (&R)[NBT],
+                                            const float (&Mt)[NBT], ESm& sm) {
   const int tid = threadIdx.x, K1 = p.K + 1, NB = p.NB, V = (int)p.V, F = p.F;
-  // the residual sums are read before the hand-over state is known (they are
-  // only used when it asks for them), so both loads are in flight together
-  float R[NBT], Mt[NBT];
-#pragma unroll
-  for (int k = 0; k < NBT; ++k) {
-    const int be = tid + k * EWG;
-    const float2 v = be < NB ? p.rpart[(int64_t)b * NB + be] : make_float2(0.f, -INFINITY);
-    R[k] = v.x;
-    Mt[k] = v.y;
-  }
-  if (!ss.need) return;
   const int ks = ss.kstar;
   const int64_t row = (int64_t)b * K1 + ks;
   const int64_t rs = p.ld * Dt<DT>::SZ;
@@ -982,7 +985,10 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
       return zt[e] > -INFINITY ? (Mb - zt[e]) * s : INFINITY;
     });
   }
-  if (tid == 0) p.bonus[b] = (x >= 0 && x < V) ? x : 0;
+  if (tid == 0) {
+    p.bonus[b] = (x >= 0 && x < V) ? x : 0;
+    sm.bonus = (x >= 0 && x < V) ? x : 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1054,12 +1060,56 @@ __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(
   else accept_residual<DT, AL, NBL>(p, b, chunk, sm);
 }
 
+// Look (k, y) up among sequence b's keys at depth k (wave 0; every lane
+// calls): lowest matching slot, its payload, or a miss.
+__device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k, int y) {
+  const int lane = threadIdx.x & 63, K = p.K, Bgt = p.Bgt;
+  int found = -1;
+  if (k >= 0 && k <= K) {
+    const int lo = p.koff[k], hi = p.koff[k + 1];
+    for (int s0 = lo; s0 < hi; s0 += 64) {
+      const int sl = s0 + lane;
+      const uint64_t m = __ballot(sl < hi && p.ckeys[(int64_t)b * Bgt + min(sl, hi - 1)] == y);
+      if (m) {
+        found = s0 + __builtin_ctzll(m);
+        break;
+      }
+    }
+  }
+  if (lane == 0) {
+    p.chit[b] = found >= 0;
+    p.cslot[b] = found;
+  }
+  for (int i = lane; i < K; i += 64)
+    p.ctok[(int64_t)b * K + i] = found >= 0 ? p.cpay[((int64_t)b * Bgt + found) * K + i] : -1;
+}
+
+// Bonus from the residual for the sequences that need it, then (when asked)
+// the cache lookup of every sequence's (k*, bonus).
 template <int DT, bool AL>
 __global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
   __shared__ ESm sm;
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, NB = p.NB;
+  // the residual sums (used only when the state asks for them), the state,
+  // and the outcome of sequences decided earlier are loaded together
+  float R[NBT], Mt[NBT];
+#pragma unroll
+  for (int k = 0; k < NBT; ++k) {
+    const int be = threadIdx.x + k * EWG;
+    const float2 v = be < NB ? p.rpart[(int64_t)b * NB + be] : make_float2(0.f, -INFINITY);
+    R[k] = v.x;
+    Mt[k] = v.y;
+  }
   const SeqState ss = p.state[b];
-  epi_residual<DT, AL>(p, b, ss, sm);
+  const int ks0 = p.lookup ? p.acc_len[b] : 0, y0 = p.lookup ? p.bonus[b] : 0;
+  if (ss.need) epi_residual<DT, AL>(p, b, ss, R, Mt, sm);
+  if (!p.lookup) return;
+  if (ss.need) {
+    __syncthreads();
+    if (threadIdx.x < 64) cache_lookup_wave(p, b, ss.kstar, sm.bonus);
+  } else if (threadIdx.x < 64) {
+    cache_lookup_wave(p, b, ks0, y0);
+  }
 }
 
 // Dense probabilities for ssd_softmax_t (after the statistics kernel).

@@ -97,6 +97,20 @@ bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
 
 const int64_t kMaxGrid = 0x7fffffff;
 
+// Depth offsets of a cache descriptor into p (false for a bad fan-out).
+bool cache_layout(const ssd_cache* c, int K, int64_t V, Params& p) {
+  int off = 0;
+  for (int k = 0; k <= K; ++k) {
+    const int f = c->fanout[k];
+    if (f < 0 || f > SSD_MAX_F || f > V) return false;
+    p.koff[k] = off;
+    off += f;
+  }
+  p.koff[K + 1] = off;
+  p.Bgt = off;
+  return true;
+}
+
 // Kernel timer: event pairs around the streaming-pass launches, per op.
 struct Timer {
   int cap = 0;
@@ -210,21 +224,25 @@ ssd_status ssd_topf(const void* logits, ssd_dtype dt, int64_t rows, int64_t V, i
 ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K, int64_t V,
                               int64_t ld, const float* temperature, int32_t F, float C, int32_t F_out,
                               uint64_t seed, int32_t* out_tokens, float* out_q, ssd_row_stats* out_stats,
-                              int32_t* out_topf_idx, float* out_topf_val, void* workspace,
-                              size_t ws_bytes, void* stream) {
+                              int32_t* out_topf_idx, float* out_topf_val, const ssd_cache* cache,
+                              void* workspace, size_t ws_bytes, void* stream) {
   if (!draft_logits || !temperature || !out_stats || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
   if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
   if (K > 0 && (!out_tokens || !out_q)) return SSD_ERR_INVALID_ARG;
   if (F < 0 || F > SSD_MAX_F || F > V || F_out < F || F_out > SSD_MAX_F || F_out > V) return SSD_ERR_INVALID_ARG;
   if (F_out > 0 && !out_topf_idx && !out_topf_val) return SSD_ERR_INVALID_ARG;
   if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
+  Params p{};
+  if (cache) {
+    if (!cache->fanout || !cache->keys || !cache_layout(cache, K, V, p)) return SSD_ERR_INVALID_ARG;
+    p.ckeys = cache->keys;
+  }
   Layout L;
   if (!layout(SSD_OP_SAMPLE, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
   if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
   const int64_t rows = (int64_t)B * (K + 1);
   const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
   if (rows * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
-  Params p{};
   p.x = (const unsigned char*)draft_logits;
   p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
   p.K = K; p.B = B;
@@ -252,8 +270,8 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
                       int64_t V, int64_t ld, const float* temperature, int32_t F, float C, uint64_t seed,
                       const int32_t* draft_tokens, const float* draft_q, const ssd_row_stats* draft_stats,
                       const int32_t* draft_topf_idx, int32_t ld_topf, int32_t* out_accept_len,
-                      int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, void* workspace,
-                      size_t ws_bytes, void* stream) {
+                      int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, const ssd_cache* cache,
+                      void* workspace, size_t ws_bytes, void* stream) {
   if (!target_logits || !draft_logits || !temperature || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
   if (!draft_stats || !out_accept_len || !out_bonus) return SSD_ERR_INVALID_ARG;
   if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
@@ -261,13 +279,25 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   if (F < 0 || F > SSD_MAX_F || F > V) return SSD_ERR_INVALID_ARG;
   if (F > 0 && (!draft_topf_idx || ld_topf < F)) return SSD_ERR_INVALID_ARG;
   if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
+  Params p{};
+  if (cache) {
+    if (!cache->fanout || !cache_layout(cache, K, V, p)) return SSD_ERR_INVALID_ARG;
+    if (p.Bgt > 0 && !cache->keys) return SSD_ERR_INVALID_ARG;
+    if (!cache->out_hit || !cache->out_slot || (K > 0 && !cache->out_tokens)) return SSD_ERR_INVALID_ARG;
+    if (K > 0 && p.Bgt > 0 && !cache->payload) return SSD_ERR_INVALID_ARG;
+    p.ckeys = cache->keys;
+    p.cpay = cache->payload;
+    p.chit = cache->out_hit;
+    p.cslot = cache->out_slot;
+    p.ctok = cache->out_tokens;
+    p.lookup = 1;
+  }
   Layout L;
   if (!layout(SSD_OP_VERIFY, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
   if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
   const int64_t rows = (int64_t)B * (K + 1);
   const int64_t NB = nblocks(V), nch = cdiv(NB, CH), nchr = cdiv(NB, CH_R);
   if (rows * nch > kMaxGrid || (int64_t)B * nchr > kMaxGrid) return SSD_ERR_UNSUPPORTED;
-  Params p{};
   p.x = (const unsigned char*)target_logits;
   p.xd = (const unsigned char*)draft_logits;
   p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;

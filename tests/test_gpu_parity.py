@@ -197,3 +197,45 @@ def test_cache_lookup_against_oracle():
     assert np.array_equal(slot.cpu().numpy(), os_)
     assert np.array_equal(toks.cpu().numpy(), ot)
     assert oh.sum() >= hits.numel() - 1
+
+
+def test_cache_keys_from_sampling_and_lookup_in_verify():
+    """The cache descriptor path: sampling writes each row's top-F_j list into
+    the depth-major keys, verification looks (k*, bonus) up in the kernel that
+    draws the bonus.  Keys bit-exact against the oracle's top lists; lookup
+    against the oracle's lookup on the GPU's (k*, bonus); every other output
+    identical to the calls without a cache."""
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    B, K, V = 8, 5, 128256
+    cfg = W.custom(B, K, V, BF16, T=0.7, F=4, C=0.6, kind="peaks", draft_sd=0.8, F_out=4, Bgt=64, ratio=0.6)
+    Fk = ssd.fanout(64, K, 0.6, V)
+    for step in range(3):
+        _say(f"cache path step {step}")
+        t, d = W.logits(cfg, step, DEV)
+        T = W.temperatures(cfg, DEV)
+        seed = W.seed(cfg, step)
+        payload = W.payload(cfg, 64, step, DEV)
+        cache = ssd.Cache(Fk, B, K, DEV, payload=payload)
+        s1 = ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=4, cache=cache)
+        s0 = ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=4)
+        v1 = ssd.verify(t, d, T, cfg.F, cfg.C, seed, s1["tokens"], s1["q"], s1["stats"], s1["topf_idx"], cache=cache)
+        v0 = ssd.verify(t, d, T, cfg.F, cfg.C, seed, s0["tokens"], s0["q"], s0["stats"], s0["topf_idx"])
+        torch.cuda.synchronize()
+        for k in ("tokens", "q", "stats", "topf_idx", "topf_val"):
+            assert torch.equal(s1[k], s0[k]), k
+        for k in ("accept_len", "bonus", "p"):
+            assert torch.equal(v1[k], v0[k]), k
+        zd = O.decode(d.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+        lists = np.zeros((B, K + 1, max(Fk)), dtype=np.int64)
+        for b in range(B):
+            for j in range(K + 1):
+                lists[b, j, :Fk[j]] = O.topf(zd[b, j], Fk[j])[0]
+        ok_keys, off = O.build_keys(lists, Fk)
+        assert np.array_equal(cache.keys.cpu().numpy(), ok_keys)
+        oh, os_, ot = O.cache_lookup(ok_keys, off, payload.cpu().numpy(), v1["accept_len"].cpu().numpy(),
+                                     v1["bonus"].cpu().numpy())
+        assert np.array_equal(cache.hit.cpu().numpy(), oh)
+        assert np.array_equal(cache.slot.cpu().numpy(), os_)
+        assert np.array_equal(cache.tokens.cpu().numpy(), ot)
+        _say(f"  hits {int(oh.sum())} of {B}")

@@ -100,28 +100,53 @@ def test_entry_points_reject_invalid_arguments_on_host(L):
     smp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_uint64,
                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-    ok = dict(B=2, K=3, V=100, ld=100, F=2, C=0.5, Fo=2)
+                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    ok = dict(B=2, K=3, V=100, ld=100, F=2, C=0.5, Fo=2, cache=None)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return smp(P, 1, a["B"], a["K"], a["V"], a["ld"], P, a["F"], a["C"], a["Fo"], 0, P, P, P, P, P, P,
-                   1 << 24, N)
+        return smp(P, 1, a["B"], a["K"], a["V"], a["ld"], P, a["F"], a["C"], a["Fo"], 0, P, P, P, P, P,
+                   a["cache"], P, 1 << 24, N)
 
     assert call(C=0.0) == 1 and call(C=1.5) == 1 and call(C=float("nan")) == 1
     assert call(B=0) == 1 and call(K=-1) == 1 and call(K=33) == 1
     assert call(Fo=1) == 1            # F_out < F
     assert call(F=65, Fo=65) == 1
+    import lossless_verify_sample_amd as ssd
+
+    def cache(fan, keys=P):
+        arr = (ctypes.c_int32 * len(fan))(*fan)
+        st = ssd._CacheStruct(ctypes.cast(arr, ctypes.c_void_p), keys, P, P, P, P)
+        st._keep = arr
+        return st
+    assert call(cache=ctypes.byref(cache([1, 2, 65, 1]))) == 1    # F_k > SSD_MAX_F
+    assert call(cache=ctypes.byref(cache([1, -1, 2, 1]))) == 1    # negative F_k
+    assert call(V=10, ld=10, cache=ctypes.byref(cache([11, 1, 1, 1]))) == 1  # F_k > V
+    assert call(cache=ctypes.byref(cache([1, 2, 3, 1], keys=None))) == 1     # no keys
     v = L.ssd_verify
     v.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                  ctypes.c_size_t, ctypes.c_void_p]
-    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 1, P, P, P, N, P, 1 << 24, N) == 1  # ld_topf < F
-    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, N, P, 2, P, P, P, N, P, 1 << 24, N) == 1  # no stats
-    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, N, P, P, 2, P, P, P, N, P, 1 << 24, N) == 1  # no q
-    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, N, P, 16, N) == 3       # small ws
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 1, P, P, P, N, N, P, 1 << 24, N) == 1  # ld_topf < F
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, N, P, 2, P, P, P, N, N, P, 1 << 24, N) == 1  # no stats
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, N, P, P, 2, P, P, P, N, N, P, 1 << 24, N) == 1  # no q
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, N, N, P, 16, N) == 3       # small ws
+    c = cache([1, 2, 3, 1])
+    c.payload = None
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, N, ctypes.byref(c), P, 1 << 24,
+             N) == 1  # cache without payload
+    c = cache([1, 2, 3, 1])
+    c.out_tokens = None
+    assert v(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, N, ctypes.byref(c), P, 1 << 24,
+             N) == 1  # cache without token outputs
+    te = L.ssd_timer_enable
+    te.argtypes = [ctypes.c_int32]
+    assert te(-1) == 1 and te((1 << 20) + 1) == 1
+    tr = L.ssd_timer_read
+    tr.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert tr(9, P, P) == 1 and tr(2, N, P) == 1
     lk = L.ssd_cache_lookup
     lk.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6
     assert lk(P, N, P, 4, 3, 8, P, P, P, P, P, N) == 1   # no depth offsets
