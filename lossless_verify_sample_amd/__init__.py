@@ -184,9 +184,10 @@ _WS = {}
 
 
 def _workspace(op, n, K, V, dev):
-    """Workspace cached per (op, shape, device) and reused (its contents do
-    not matter).  Calls sharing one must not overlap."""
-    key = (op, n, K, V, dev)
+    """Workspace cached per (op, shape, device, current stream) and reused
+    (its contents do not matter): calls of one op on one stream are ordered
+    by that stream, and calls on different streams get different buffers."""
+    key = (op, n, K, V, dev, torch.cuda.current_stream(dev).cuda_stream)
     w = _WS.get(key)
     if w is None:
         nb = workspace_bytes(op, n, K, V)
