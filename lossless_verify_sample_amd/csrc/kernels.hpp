@@ -31,6 +31,7 @@ constexpr int TPT = BLK / EWG;    // tokens per epilogue thread in a token stage
 constexpr int NBT = MAX_NB / EWG; // blocks per epilogue thread
 constexpr int NBL = MAX_NB / 64;  // blocks per lane when a wave holds a whole row
 static_assert(TPT == 8 && NBT == 2, "epilogue layout assumes 256 threads over 2048-token blocks");
+constexpr int TF_CAP = EWG;       // (K+1)*F draft top-F entries prefetched into LDS when they fit
 
 // What verification hands to the residual pass for one sequence.
 struct SeqState {
@@ -79,6 +80,8 @@ struct Params {
   // speculation cache (optional): depth offsets, keys, payload, lookup outputs
   int koff[MAX_K1 + 1];
   int Bgt;
+  int kdep[MAX_K1];         // sampling: depths whose key list is longer than F_sel, each ranked by
+  int nkd;                  // B extra workgroups of the epilogue (after the B (K+1) row workgroups)
   int lookup;               // verification looks (k*, bonus) up
   int32_t* ckeys;           // [B, Bgt]; sampling writes, verification reads
   const int32_t* cpay;      // [B, Bgt, K]
@@ -96,9 +99,11 @@ struct ESm {
   float M[MAX_NB];          // block maxima (verification: row K; residual: target row k*)
   float S[MAX_NB];          // block sums (verification: row K)
   int cblk[MAX_NB];         // candidate blocks for top-F
+  int rblk[MAX_NB];         // candidate blocks re-read for top-F
   uint64_t cand[CAND_CAP];  // top-F candidates as (value desc, index asc) keys
   uint64_t tkey[MAX_F];     // top-F result through LDS, sorted
   uint64_t wk[ENW][64];     // each wave's own top-F exchange row
+  int tf[TF_CAP];           // verification: the draft top-F lists of a sequence's rows
   int nre;                  // candidates appended by block re-reads
   int ks;
   int bonus;
@@ -301,35 +306,41 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&key)[PLN], int Fs, 
 }
 
 // Exact top-Fs of a row (value desc, index asc) from a wave's copy of its
-// partials.  tau, the Fs-th largest block maximum, bounds the Fs-th largest
-// element from below, so every top element lies in a candidate block (maximum
-// >= tau).  A candidate whose second value is below tau holds exactly one
-// element >= tau, its maximum, whose index the partial carries.  When every
+// partials.  The block maxima and second values are values of 2 NB distinct
+// elements, so tau, the Fs-th largest of them, bounds the Fs-th largest
+// element from below, and every top element lies in a candidate block
+// (maximum >= tau).  A candidate whose second value is below tau holds
+// exactly one element >= tau, its maximum, whose index the partial carries.  When every
 // candidate is of that kind (the common case) each wave ranks the candidate
-// maxima itself; otherwise the other candidates are re-read (round-robin
-// over the waves) and all candidates are ranked through LDS.  On return lane
+// maxima itself; otherwise the other candidates are re-read by the whole
+// workgroup (each thread one 16-byte chunk of each) and all candidates are
+// ranked through LDS.  On return lane
 // r < Fs of every wave holds entry r as a (value, index) key, 0 elsewhere.
 // Every wave of the workgroup calls; sm.nre must have been cleared at start.
 template <int DT, bool AL, int PLN>
 __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, int NB, int Fs, const WRow<PLN>& r,
                                               float m, ESm& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t key[PLN];
+  // the block maxima and second values: 2 NB values of distinct elements
+  // (a second value of -inf in a one-element block stands for none)
+  uint32_t key[2 * PLN];
   uint32_t kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int i = 0; i < PLN; ++i) {
     const bool in = lane + 64 * i < NB;
     key[i] = in ? ord_key(r.M[i]) : 0u;
-    kmin = in ? min(kmin, key[i]) : kmin;
+    key[PLN + i] = in ? ord_key(r.M2[i]) : 0u;
+    kmin = in ? min(kmin, key[PLN + i]) : kmin;
   }
-  const uint32_t tk = NB > Fs ? kth_key<PLN>(key, Fs, ord_key(m), wave_min_u32(kmin), LowBit<DT>::B) : 0u;
-  const float tau = NB > Fs ? ord_val(tk) : -INFINITY;
+  const bool sel = 2 * NB > Fs;
+  const uint32_t tk = sel ? kth_key<2 * PLN>(key, Fs, ord_key(m), wave_min_u32(kmin), LowBit<DT>::B) : 0u;
+  const float tau = sel ? ord_val(tk) : -INFINITY;
   bool cand[PLN], one[PLN];
   uint64_t more = 0;
 #pragma unroll
   for (int i = 0; i < PLN; ++i) {
     cand[i] = lane + 64 * i < NB && key[i] >= tk;
-    one[i] = cand[i] && NB > Fs && r.M2[i] < tau;
+    one[i] = cand[i] && sel && r.M2[i] < tau;
     more |= __ballot(cand[i] && !one[i]);
   }
   if (more == 0) {
@@ -361,38 +372,48 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     return lane < Fs ? wk[lane] : 0ull;
   }
-  // general case: wave 0 lists the candidate blocks and the one-element
-  // candidates; the other candidates are re-read round-robin
+  // general case: wave 0 lists the candidate blocks, the blocks to re-read
+  // and the one-element candidates; then every thread scans its 16-byte
+  // chunks of the re-read blocks, RB blocks' loads in flight at a time
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
-  int n1 = 0, ncb = 0, nr = 0;
+  int n1 = 0, ncb = 0, nrb = 0;
 #pragma unroll
   for (int i = 0; i < PLN; ++i) {
     const int be = lane + 64 * i;
-    const uint64_t cm = __ballot(cand[i]), om = __ballot(one[i]);
+    const bool re = cand[i] && !one[i];
+    const uint64_t cm = __ballot(cand[i]), om = __ballot(one[i]), rm = __ballot(re);
     if (wave == 0) {
       if (cand[i]) sm.cblk[ncb + __popcll(cm & below)] = be;
+      if (re) sm.rblk[nrb + __popcll(rm & below)] = be;
       if (one[i] && n1 + __popcll(om & below) < CAND_CAP) sm.cand[n1 + __popcll(om & below)] = vi_key(r.M[i], r.I[i]);
     }
     ncb += __popcll(cm);
     n1 += __popcll(om);
+    nrb += __popcll(rm);
   }
+  __syncthreads();
+  {
+    constexpr int VW = Dt<DT>::VW, RB = 8;
+    for (int c0 = tid; c0 < BLK / VW; c0 += EWG) {  // chunk c0 of every re-read block
+      for (int k0 = 0; k0 < nrb; k0 += RB) {
+        float v[RB][VW];
 #pragma unroll
-  for (int i = 0; i < PLN; ++i) {
-    uint64_t rr = __ballot(cand[i] && !one[i]);
-    while (rr) {
-      const int be = 64 * i + (int)__builtin_ctzll(rr);
-      rr &= rr - 1ull;
-      if (nr++ % ENW != wave) continue;
-      float v[32];
-      if ((be + 1) * BLK <= V) load_block_full<DT, AL>(rp, be, lane, v);
-      else load_block<DT, AL>(rp, V, be, lane, v);
+        for (int u = 0; u < RB; ++u) {
+          const int e0 = sm.rblk[min(k0 + u, nrb - 1)] * BLK + c0 * VW;
+          load_chunk<DT, AL>(rp, V, e0, v[u]);
+        }
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const int idx = block_elem_index<DT>(be, lane, k);
-        if (v[k] >= tau && idx < V) {
-          const int pos = n1 + atomicAdd(&sm.nre, 1);
-          if (pos < CAND_CAP) sm.cand[pos] = vi_key(v[k], idx);
+        for (int u = 0; u < RB; ++u) {
+          if (k0 + u >= nrb) break;
+          const int e0 = sm.rblk[k0 + u] * BLK + c0 * VW;
+#pragma unroll
+          for (int e = 0; e < VW; ++e) {
+            if (v[u][e] >= tau && e0 + e < V) {
+              const int pos = n1 + atomicAdd(&sm.nre, 1);
+              if (pos < CAND_CAP) sm.cand[pos] = vi_key(v[u][e], e0 + e);
+            }
+          }
         }
       }
     }
@@ -609,6 +630,8 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
   if (tid == 0) sm.nre = 0;
   const bool draw = !greedy && j < p.K;
+  WRow<PLN> r;
+  load_wrow<PLN>(p.part + row * NB, NB, r);
   // -log2(u) of every block for the block stage: independent of the logits,
   // computed while the partials load
   float E[PLN];
@@ -616,8 +639,6 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   for (int i = 0; i < PLN; ++i)
     E[i] = draw ? neg_log2_u(draw1(p.seed, (uint32_t)(lane + 64 * i), (uint32_t)b, (uint32_t)j, ST_DRAFT_BLOCK))
                 : 0.f;
-  WRow<PLN> r;
-  load_wrow<PLN>(p.part + row * NB, NB, r);
   float lm = r.M[0];
 #pragma unroll
   for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
@@ -630,9 +651,10 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
     ws += (double)w[i];
   }
   const double tot0 = greedy ? 1.0 : wave_sum_d(ws);
-  // entries ranked: F for sigma, F_out listed, and this depth's cache keys
+  // entries ranked: F for sigma and F_out listed; this depth's cache keys
+  // when they fit in that list (longer key lists have workgroups of their own)
   const int Fj = p.ckeys ? p.koff[j + 1] - p.koff[j] : 0;
-  const uint64_t tkey = wave_topf<DT, AL, PLN>(rp, V, NB, max(p.F_sel, Fj), r, m, sm);
+  const uint64_t tkey = wave_topf<DT, AL, PLN>(rp, V, NB, p.F_sel, r, m, sm);
   const float tv = key_val(tkey);
   const int ti = (int)key_idx(tkey);
   // sigma_{F,C}: lane f < F holds 2^((z_f - m) s) of the f-th member of S
@@ -644,7 +666,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
       if (p.out_idx) p.out_idx[row * p.F_out + lane] = ti;
       if (p.out_val) p.out_val[row * p.F_out + lane] = tv;
     }
-    if (lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = ti;
+    if (Fj <= p.F_sel && lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = ti;
     if (lane == 0) {
       ssd_row_stats st;
       st.lse = lse;
@@ -707,6 +729,27 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   }
 }
 
+// Cache keys of depth kdep[item / B] for sequence item % B: the first F_j
+// entries of that draft row's top list (a workgroup of its own, in parallel
+// with the row's sampling).
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ void epi_keys_p(const Params& p, int item, ESm& sm) {
+  const int b = item % p.B, j = p.kdep[item / p.B];
+  const int64_t row = (int64_t)b * (p.K + 1) + j;
+  const int Fj = p.koff[j + 1] - p.koff[j];
+  if (threadIdx.x == 0) sm.nre = 0;
+  const int NB = p.NB;
+  WRow<PLN> r;
+  load_wrow<PLN>(p.part + row * NB, NB, r);
+  float lm = r.M[0];
+#pragma unroll
+  for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+  const float m = wave_max(lm);
+  const uint64_t tk = wave_topf<DT, AL, PLN>(p.x + row * p.ld * Dt<DT>::SZ, (int)p.V, NB, Fj, r, m, sm);
+  const int lane = threadIdx.x;
+  if (lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = (int)key_idx(tk);  // wave 0: Fj <= 64
+}
+
 // Acceptance and residual pass of verification, one workgroup per (sequence,
 // chunk of CH_R blocks).  Every workgroup of a sequence merges the partials
 // of its K + 1 target rows and takes the acceptance decisions itself (the
@@ -745,6 +788,11 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     dmax = ds.max;
     dlse = ds.lse;
   }
+  // the draft top-F lists of all K + 1 rows (the residual of row k* needs
+  // one), fetched with the rest so that no load waits on k*
+  const int F = p.F;
+  const bool tf_lds = F > 0 && K1 * F <= TF_CAP;
+  if (tf_lds && tid < K1 * F) sm.tf[tid] = p.dtopf[(r0 + tid / F) * p.ld_dtopf + tid % F];
   // row statistics: wave w merges rows j = w, w + ENW, ..., two rows per pass
   // with both rows' loads in flight
   auto merge = [&](const WRow<PLN>& r, int j) {
@@ -781,11 +829,15 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
       sm.vam[j] = greedy ? (am < 0 ? 0 : am) : -1;  // greedy rows carry the block argmax in their partial
     }
   };
+  float uacc = 0.f;
   for (int j0 = wave; j0 < K1; j0 += 2 * ENW) {
     const int j1 = j0 + ENW;
     WRow<PLN> ra, rb;
     load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
     load_wrow<PLN>(p.part + (r0 + min(j1, K)) * NB, NB, rb);
+    // wave 0, lane j: the acceptance draw u_j, computed while the partials load
+    if (wave == 0 && j0 == 0 && !greedy)
+      uacc = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
     merge(ra, j0);
     if (j1 < K1) merge(rb, j1);
   }
@@ -810,8 +862,7 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
         pj = exp_fast(((double)ztj - (double)sm.vm[lane]) * invT - sm.vL[lane]);
         const double q = (double)qj;
         const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
-        const float u = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
-        acc = (double)u < rho;
+        acc = (double)uacc < rho;
       }
     }
     if (lead && lane < K) p.p_out[b * K + lane] = (float)pj;
@@ -915,11 +966,21 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
       a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
     }
     float R = wave_sum(a0 + a1);
-    // members of the draft's top-F set in this block carry the factor C
-    for (int f = 0; f < p.F; ++f) {
-      const int x = p.dtopf[rrow + f];
+    // members of the draft's top-F set in this block carry the factor C; the
+    // member's logits are element kk of lane gi & 63 in this wave's registers
+    for (int f = 0; f < F; ++f) {
+      const int x = __builtin_amdgcn_readfirstlane(tf_lds ? sm.tf[ks * F + f] : p.dtopf[rrow + f]);
       if (x >= 0 && x < V && x / BLK == be) {
-        const float zt = load_elem<DT>(rt, x), zd = load_elem<DT>(rd, x);
+        constexpr int VW = Dt<DT>::VW;
+        const int off = x - be * BLK, gi = off / VW, kk = (gi >> 6) * VW + off % VW;
+        float zt = vt[0], zd = vd[0];
+#pragma unroll
+        for (int k = 1; k < 32; ++k) {
+          zt = k == kk ? vt[k] : zt;
+          zd = k == kk ? vd[k] : zd;
+        }
+        zt = rl_f(zt, gi & 63);
+        zd = rl_f(zd, gi & 63);
         const float e1 = __builtin_amdgcn_exp2f(fmaf(zt, s, ot));
         const float e2 = __builtin_amdgcn_exp2f(fmaf(zd, s, od));
         R += fmaxf(fmaf(nk * p.C, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
@@ -933,7 +994,7 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
 
 template <int DT, bool AL>
 __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqState& ss, const float (&R)[NBT],
-                                            const float (&Mt)[NBT], ESm& sm) {
+                                            const float (&Mt)[NBT], bool tf_lds, ESm& sm) {
   const int tid = threadIdx.x, K1 = p.K + 1, NB = p.NB, V = (int)p.V, F = p.F;
   const int ks = ss.kstar;
   const int64_t row = (int64_t)b * K1 + ks;
@@ -968,7 +1029,8 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
   int x = -1;
   if (any) {
     // r = p - sigma > 0 iff d = ln sigma - ln p < 0, and then r = p (-expm1(d))
-    const uint32_t smask = F > 0 ? set_mask(p.dtopf + row * p.ld_dtopf, F, x0) : 0u;
+    const uint32_t smask = F <= 0 ? 0u : tf_lds ? set_mask(sm.tf + ks * F, F, x0)
+                                                : set_mask(p.dtopf + row * p.ld_dtopf, F, x0);
     const double invT = ss.invT, D0 = ss.D0, lnC = ss.lnC;
     x = token_race(x0, V, p.seed, b, ks, ST_BONUS_TOKEN, sm.ru[1], [&](int e) -> float {
       if (!(zt[e] > -INFINITY)) return INFINITY;
@@ -1048,7 +1110,10 @@ __global__ __launch_bounds__(EWG) void k_epi(Params p) {
   const bool small = p.NB <= 128;
   if constexpr (MODE == M_SOFTMAX) small ? epi_softmax_p<DT, AL, 2>(p, g) : epi_softmax_p<DT, AL, NBL>(p, g);
   if constexpr (MODE == M_TOPF) small ? epi_topf_p<DT, AL, 2>(p, g, sm) : epi_topf_p<DT, AL, NBL>(p, g, sm);
-  if constexpr (MODE == M_SAMPLE) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
+  if constexpr (MODE == M_SAMPLE) {
+    if (g < p.rows) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
+    else small ? epi_keys_p<DT, AL, 2>(p, g - (int)p.rows, sm) : epi_keys_p<DT, AL, NBL>(p, g - (int)p.rows, sm);
+  }
 }
 
 // Acceptance and residual pass (one workgroup per sequence and chunk).
@@ -1060,10 +1125,55 @@ __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(
   else accept_residual<DT, AL, NBL>(p, b, chunk, sm);
 }
 
+// Wave 0's copy of sequence b's keys and payload, one slot per lane, when
+// they fit (Bgt <= 64, K <= KREG): fetched at kernel start so the lookup
+// needs no load once the bonus is known.
+constexpr int KREG = 8;
+struct CacheRegs {
+  bool ok;
+  int key;
+  int pay[KREG];
+};
+
+__device__ __forceinline__ void cache_prefetch(const Params& p, int b, CacheRegs& cr) {
+  const int lane = threadIdx.x & 63, K = p.K, Bgt = p.Bgt;
+  cr.ok = p.lookup && Bgt <= 64 && K <= KREG;
+  cr.key = 0;
+#pragma unroll
+  for (int i = 0; i < KREG; ++i) cr.pay[i] = -1;
+  if (!cr.ok || threadIdx.x >= 64 || lane >= Bgt) return;
+  const int64_t sl = (int64_t)b * Bgt + lane;
+  cr.key = p.ckeys[sl];
+#pragma unroll
+  for (int i = 0; i < KREG; ++i)
+    if (i < K) cr.pay[i] = p.cpay[sl * K + i];
+}
+
 // Look (k, y) up among sequence b's keys at depth k (wave 0; every lane
 // calls): lowest matching slot, its payload, or a miss.
-__device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k, int y) {
+__device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k, int y, const CacheRegs& cr) {
   const int lane = threadIdx.x & 63, K = p.K, Bgt = p.Bgt;
+  if (cr.ok) {
+    int found = -1;
+    if (k >= 0 && k <= K) {
+      const uint64_t m = __ballot(lane >= p.koff[k] && lane < p.koff[k + 1] && cr.key == y);
+      if (m) found = (int)__builtin_ctzll(m);
+    }
+    if (lane == 0) {
+      p.chit[b] = found >= 0;
+      p.cslot[b] = found;
+    }
+    int t = -1;
+    if (found >= 0) {
+#pragma unroll
+      for (int i = 0; i < KREG; ++i) {
+        const int v = __builtin_amdgcn_readlane(cr.pay[i], found);
+        t = lane == i ? v : t;
+      }
+    }
+    if (lane < K) p.ctok[(int64_t)b * K + lane] = t;
+    return;
+  }
   int found = -1;
   if (k >= 0 && k <= K) {
     const int lo = p.koff[k], hi = p.koff[k + 1];
@@ -1102,13 +1212,20 @@ __global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
   }
   const SeqState ss = p.state[b];
   const int ks0 = p.lookup ? p.acc_len[b] : 0, y0 = p.lookup ? p.bonus[b] : 0;
-  if (ss.need) epi_residual<DT, AL>(p, b, ss, R, Mt, sm);
+  CacheRegs cr;
+  cache_prefetch(p, b, cr);
+  // the draft top-F lists of all rows, for the residual's sigma (row k*)
+  const int K1 = p.K + 1, F = p.F;
+  const bool tf_lds = F > 0 && K1 * F <= TF_CAP;
+  if (tf_lds && threadIdx.x < K1 * F)
+    sm.tf[threadIdx.x] = p.dtopf[((int64_t)b * K1 + threadIdx.x / F) * p.ld_dtopf + threadIdx.x % F];
+  if (ss.need) epi_residual<DT, AL>(p, b, ss, R, Mt, tf_lds, sm);
   if (!p.lookup) return;
   if (ss.need) {
     __syncthreads();
-    if (threadIdx.x < 64) cache_lookup_wave(p, b, ss.kstar, sm.bonus);
+    if (threadIdx.x < 64) cache_lookup_wave(p, b, ss.kstar, sm.bonus, cr);
   } else if (threadIdx.x < 64) {
-    cache_lookup_wave(p, b, ks0, y0);
+    cache_lookup_wave(p, b, ks0, y0, cr);
   }
 }
 

@@ -248,6 +248,10 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
   p.K = K; p.B = B;
   p.temp = temperature;
   p.F = F; p.F_out = F_out; p.F_sel = F_out > 1 ? F_out : 1;
+  if (cache) {
+    for (int j = 0; j <= K; ++j)
+      if (cache->fanout[j] > p.F_sel) p.kdep[p.nkd++] = j;
+  }
   p.C = C; p.seed = seed;
   char* ws = (char*)workspace;
   p.part = (float4*)(ws + L.part);
@@ -262,7 +266,7 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
   hipError_t e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
     return dispatch<LSample>(dt, al, rows * nch, p, st, e0, e1);
   });
-  if (e == hipSuccess) e = dispatch<LSampleEpi>(dt, al, rows, p, st);
+  if (e == hipSuccess) e = dispatch<LSampleEpi>(dt, al, rows + (int64_t)p.nkd * B, p, st);
   return hip_status(e);
 }
 
