@@ -112,7 +112,9 @@ typedef struct {
  *   payload    device int32 [B, Bgt, K]: the K pre-speculated tokens of a slot
  *              (ssd_verify; may be NULL when K = 0)
  *   out_hit, out_slot  device int32 [B]; out_tokens device int32 [B, K]
- *              (ssd_verify): as ssd_cache_lookup. */
+ *              (ssd_verify): as ssd_cache_lookup.
+ *   miss_fill  0 or 1 (ssd_verify): as ssd_cache_lookup, with the call's V
+ *              and seed. */
 typedef struct {
   const int32_t* fanout;
   int32_t* keys;
@@ -120,6 +122,7 @@ typedef struct {
   int32_t* out_hit;
   int32_t* out_slot;
   int32_t* out_tokens;
+  int32_t miss_fill;
 } ssd_cache;
 
 /* Temperature softmax row statistics ([SSD-A] and [SSD-B] part 2 name the
@@ -222,11 +225,20 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
  *   payload   device int32 [B, Bgt, K]: the K pre-speculated tokens of a slot
  *   accept_len, bonus  device int32 [B] (from ssd_verify)
  * Outputs (device): out_hit int32 [B] (1/0); out_slot int32 [B] (lowest
- * matching slot or -1); out_tokens int32 [B, K] (payload or -1).
- * An accepted length outside [0, K] or offsets out of order give a miss. */
+ * matching slot or -1); out_tokens int32 [B, K] (payload on a hit).
+ * On a miss ([SSD-B] part 3: past a critical batch size a miss is served by
+ * a near-zero-latency speculator such as random tokens): miss_fill = 0 writes
+ * -1 (the caller runs its own backup speculator); miss_fill = 1 writes K
+ * random tokens in [0, V): token i of sequence b is floor(w * V / 2^32) with
+ * w the Philox word of stream 5 at (idx = i, b, j = 0) under `seed` (V and
+ * seed are read only when miss_fill = 1).
+ * An accepted length outside [0, K] or offsets out of order give a miss.
+ * Errors: also miss_fill not 0 or 1, or miss_fill = 1 with V outside
+ * [1, SSD_MAX_V]. */
 ssd_status ssd_cache_lookup(const int32_t* keys, const int32_t* depth_off, const int32_t* payload, int32_t B,
                             int32_t K, int32_t Bgt, const int32_t* accept_len, const int32_t* bonus,
-                            int32_t* out_hit, int32_t* out_slot, int32_t* out_tokens, void* stream);
+                            int32_t* out_hit, int32_t* out_slot, int32_t* out_tokens, int32_t miss_fill,
+                            int64_t V, uint64_t seed, void* stream);
 
 /* Build cache keys from per-row top-F lists: keys[b, depth_off[k] + i] =
  * topf_idx[b, k, i] for i < F_k = depth_off[k+1] - depth_off[k] (F_k <=
@@ -246,6 +258,35 @@ ssd_status ssd_cache_keys(const int32_t* topf_idx, int32_t ld_topf, const int32_
  *   out_F host int32 [K+1].  Errors: Bgt < 0, K < 0 or > SSD_MAX_K, ratio not
  *   finite or <= 0, V < 1, Bgt > (K+1)*V. */
 ssd_status ssd_fanout(int32_t Bgt, int32_t K, double ratio, int64_t V, int32_t* out_F);
+
+/* Back-off rule for cache misses ([SSD-B] part 3: as the batch grows, the
+ * chance that some sequence misses grows and the whole batch waits for the
+ * backup speculator; below a critical batch size, set by the hit rate and the
+ * latencies, an accurate slow backup pays, above it a near-zero-latency one
+ * such as random tokens).  The pages give no formula; this rule compares
+ * expected tokens per unit time.  With P = prod_b p_hit[b], the chance that
+ * no sequence misses:
+ *   accurate backup: B * e_acc tokens per t_round + (1 - P) * t_slow;
+ *   fast backup:     sum_b (p_b e_acc + (1 - p_b) e_fast) tokens per
+ *                    t_round + (1 - P) * t_fast.
+ * Pure host function.
+ *   p_hit  host double [B], each in [0, 1] (e.g. measured per-sequence hit
+ *          rates)
+ *   c      t_round > 0, t_slow >= 0, t_fast >= 0 (any one time unit),
+ *          e_acc > 0, e_fast >= 0 (tokens per sequence and round), all finite
+ * Outputs: *out_use_fast = 1 when the fast backup's rate is strictly higher
+ * (else 0); *out_gain = its rate over the accurate backup's (out_gain may be
+ * NULL).  Errors: SSD_ERR_INVALID_ARG for B < 1, null pointers or values out
+ * of range. */
+typedef struct {
+  double t_round;  /* a round in which every sequence hits */
+  double t_slow;   /* added wait for the accurate backup speculator */
+  double t_fast;   /* added wait for the fast backup (random tokens) */
+  double e_acc;    /* tokens per sequence and round from an accurate speculation */
+  double e_fast;   /* tokens per sequence and round from the fast backup */
+} ssd_backoff_cost;
+ssd_status ssd_backoff(const double* p_hit, int32_t B, const ssd_backoff_cost* c, int32_t* out_use_fast,
+                       double* out_gain);
 
 /* Workspace bytes for `op`.  n = rows for SOFTMAX_T / TOPF (K ignored), n = B
  * for SAMPLE / VERIFY.  Returns 0 for invalid sizes. */

@@ -15,7 +15,7 @@ import torch  # provides the process's HIP runtime, which libssd then shares
 
 __all__ = [
     "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "cache_keys", "cache_lookup",
-    "fanout", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
+    "fanout", "backoff", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
@@ -34,16 +34,23 @@ class SSDError(RuntimeError):
 
 class _CacheStruct(ctypes.Structure):
     _fields_ = [("fanout", _vp), ("keys", _vp), ("payload", _vp), ("out_hit", _vp), ("out_slot", _vp),
-                ("out_tokens", _vp)]
+                ("out_tokens", _vp), ("miss_fill", ctypes.c_int32)]
+
+
+class _BackoffCost(ctypes.Structure):
+    _fields_ = [("t_round", ctypes.c_double), ("t_slow", ctypes.c_double), ("t_fast", ctypes.c_double),
+                ("e_acc", ctypes.c_double), ("e_fast", ctypes.c_double)]
 
 
 class Cache:
     """Speculation-cache descriptor (ssd_cache): the per-depth fan-out (host
     ints, e.g. from fanout()), the depth-major keys [B, Bgt] that sampling
     writes, and for verification the payload [B, Bgt, K] and the lookup
-    outputs hit [B], slot [B], tokens [B, K] (allocated when not given)."""
+    outputs hit [B], slot [B], tokens [B, K] (allocated when not given).
+    miss_fill: a miss gets random fallback tokens instead of -1."""
 
-    def __init__(self, fanout, B, K, device, payload=None, keys=None, hit=None, slot=None, tokens=None):
+    def __init__(self, fanout, B, K, device, payload=None, keys=None, hit=None, slot=None, tokens=None,
+                 miss_fill=False):
         self.fanout = [int(f) for f in fanout]
         if len(self.fanout) != K + 1:
             raise SSDError("fanout must have K+1 entries")
@@ -60,6 +67,7 @@ class Cache:
         for f in self.fanout:
             off.append(off[-1] + f)
         self.depth_off = torch.tensor(off, **i32)
+        self.miss_fill = bool(miss_fill)
 
     def _struct(self, dev, verify):
         _need(self.keys, torch.int32, "cache keys", dev)
@@ -75,6 +83,7 @@ class Cache:
             for t, n in ((self.hit, "hit"), (self.slot, "slot"), (self.tokens, "tokens")):
                 _need(t, torch.int32, "cache " + n, dev)
             st.out_hit, st.out_slot, st.out_tokens = _p(self.hit), _p(self.slot), _p(self.tokens)
+            st.miss_fill = 1 if self.miss_fill else 0
         return st
 
 
@@ -89,7 +98,8 @@ def _load():
                                _vp, _vp, _vp, _vp, _sz, _vp],
         "ssd_verify": [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _vp, _i32, _f32, _u64, _vp, _vp, _vp, _vp, _i32,
                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
-        "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+        "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _u64, _vp],
+        "ssd_backoff": [_vp, _i32, _vp, _vp, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
     }
@@ -318,8 +328,9 @@ def cache_keys(topf_idx, depth_off, Bgt):
     return keys
 
 
-def cache_lookup(keys, depth_off, payload, accept_len, bonus):
-    """(hit [B], slot [B], tokens [B, K]) int32 for the realised (accepted length, bonus)."""
+def cache_lookup(keys, depth_off, payload, accept_len, bonus, miss_fill=False, V=0, seed=0):
+    """(hit [B], slot [B], tokens [B, K]) int32 for the realised (accepted length, bonus).
+    A miss gets -1 tokens, or with miss_fill K random tokens in [0, V) keyed by seed."""
     _need(keys, torch.int32, "keys")
     dev = keys.device
     for t, n in ((depth_off, "depth_off"), (payload, "payload"), (accept_len, "accept_len"), (bonus, "bonus")):
@@ -332,8 +343,22 @@ def cache_lookup(keys, depth_off, payload, accept_len, bonus):
     slot = torch.empty(B, dtype=torch.int32, device=dev)
     toks = torch.empty((B, K), dtype=torch.int32, device=dev)
     _check(_lib.ssd_cache_lookup(_p(keys), _p(depth_off), _p(payload), B, K, Bgt, _p(accept_len), _p(bonus),
-                                 _p(hit), _p(slot), _p(toks), _stream(dev)), "ssd_cache_lookup")
+                                 _p(hit), _p(slot), _p(toks), 1 if miss_fill else 0, int(V),
+                                 int(seed) & (2 ** 64 - 1), _stream(dev)), "ssd_cache_lookup")
     return hit, slot, toks
+
+
+def backoff(p_hit, t_round, t_slow, t_fast, e_acc, e_fast):
+    """(use_fast, gain): whether misses should get the fast backup (random
+    tokens) rather than the accurate one, and its throughput ratio (host
+    computation in libssd)."""
+    p = [float(x) for x in p_hit]
+    arr = (ctypes.c_double * len(p))(*p)
+    c = _BackoffCost(float(t_round), float(t_slow), float(t_fast), float(e_acc), float(e_fast))
+    use = ctypes.c_int32(0)
+    gain = ctypes.c_double(0.0)
+    _check(_lib.ssd_backoff(arr, len(p), ctypes.byref(c), ctypes.byref(use), ctypes.byref(gain)), "ssd_backoff")
+    return bool(use.value), gain.value
 
 
 def fanout(Bgt, K, ratio, V):

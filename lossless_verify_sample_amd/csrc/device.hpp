@@ -439,6 +439,14 @@ __device__ __forceinline__ uint32_t draw1(uint64_t seed, uint32_t idx, uint32_t 
   const uint32_t s = idx & 3u;
   return s == 0 ? w.x : s == 1 ? w.y : s == 2 ? w.z : w.w;
 }
+// A token in [0, V) from a word: the high half of w * V.
+__device__ __forceinline__ int token_of_word(uint32_t w, int64_t V) {
+  return (int)(((uint64_t)w * (uint64_t)V) >> 32);
+}
+// Token i of the random stand-in for sequence b's missed cache entry.
+__device__ __forceinline__ int fallback_token(uint64_t seed, int b, int i, int64_t V) {
+  return token_of_word(draw1(seed, (uint32_t)i, (uint32_t)b, 0u, ST_FALLBACK), V);
+}
 // u = ((w >> 9) + 0.5) * 2^-23: an odd multiple of 2^-24, exact in binary32.
 __device__ __forceinline__ float uniform_of(uint32_t w) {
   return (float)(((w >> 9) << 1) | 1u) * 5.9604644775390625e-8f;  // 2^-24

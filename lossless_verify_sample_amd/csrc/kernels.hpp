@@ -80,6 +80,7 @@ struct Params {
   // speculation cache (optional): depth offsets, keys, payload, lookup outputs
   int koff[MAX_K1 + 1];
   int Bgt;
+  int fill;                 // verification: a miss gets the random fallback tokens (else -1)
   int kdep[MAX_K1];         // sampling: depths whose key list is longer than F_sel, each ranked by
   int nkd;                  // B extra workgroups of the epilogue (after the B (K+1) row workgroups)
   int lookup;               // verification looks (k*, bonus) up
@@ -1064,18 +1065,11 @@ __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(P
   const int chunk = item - (int)(row * p.nchunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K1 = p.K + 1;
-  float T = 0.f;
-  if constexpr (MODE == M_SOFTMAX) T = p.temp[row];
-  if constexpr (MODE == M_SAMPLE || MODE == M_VERIFY) T = p.temp[row / K1];
-  const float s = (T > 0.f) ? (float)(LOG2E / (double)T) : 0.f;
   const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
   const int V = (int)p.V, NB = p.NB;
   const int b0 = chunk * CH + wave, b1 = b0 + NWAVE;
-  int xj = -1;  // verification: drafted token of this target row (j < K)
-  if constexpr (MODE == M_VERIFY) {
-    const int j = (int)(row % K1);
-    if (j < p.K) xj = p.dtok[(row / K1) * p.K + j];
-  }
+  // the logit loads are issued first; the temperature (and the drafted
+  // token) are fetched behind them
   RawBlock<DT, AL> r0, r1;
   const bool full = (chunk + 1) * CH * BLK <= V;
   if (full) {
@@ -1086,6 +1080,16 @@ __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(P
     // the chunk holding the ragged end of the row
     load_raw<DT, AL, false>(rp, V, min(b0, NB - 1), lane, r0);
     load_raw<DT, AL, false>(rp, V, min(b1, NB - 1), lane, r1);
+  }
+  float T = 0.f;
+  if constexpr (MODE == M_SOFTMAX) T = p.temp[row];
+  if constexpr (MODE == M_SAMPLE || MODE == M_VERIFY) T = p.temp[row / K1];
+  const double sd = LOG2E / (double)T;
+  const float s = (T > 0.f) ? (float)sd : 0.f;
+  int xj = -1;  // verification: drafted token of this target row (j < K)
+  if constexpr (MODE == M_VERIFY) {
+    const int j = (int)(row % K1);
+    if (j < p.K) xj = p.dtok[(row / K1) * p.K + j];
   }
   float v[32];
   decode_raw<DT, AL>(r0, v);
@@ -1170,6 +1174,8 @@ __device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k,
         const int v = __builtin_amdgcn_readlane(cr.pay[i], found);
         t = lane == i ? v : t;
       }
+    } else if (p.fill && lane < K) {
+      t = fallback_token(p.seed, b, lane, p.V);
     }
     if (lane < K) p.ctok[(int64_t)b * K + lane] = t;
     return;
@@ -1191,7 +1197,9 @@ __device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k,
     p.cslot[b] = found;
   }
   for (int i = lane; i < K; i += 64)
-    p.ctok[(int64_t)b * K + i] = found >= 0 ? p.cpay[((int64_t)b * Bgt + found) * K + i] : -1;
+    p.ctok[(int64_t)b * K + i] = found >= 0 ? p.cpay[((int64_t)b * Bgt + found) * K + i]
+                                 : p.fill   ? fallback_token(p.seed, b, i, p.V)
+                                            : -1;
 }
 
 // Bonus from the residual for the sequences that need it, then (when asked)
@@ -1266,7 +1274,8 @@ __global__ __launch_bounds__(WG) void k_probs(Params p) {
 // waits on the decision.
 __global__ __launch_bounds__(WG) void k_lookup(const int32_t* keys, const int32_t* off, const int32_t* payload,
                                                int B, int K, int Bgt, const int32_t* acc, const int32_t* bonus,
-                                               int32_t* hit, int32_t* slot, int32_t* toks) {
+                                               int32_t* hit, int32_t* slot, int32_t* toks, int64_t V,
+                                               uint64_t seed, int fill) {
   __shared__ int so[MAX_K1 + 1];
   if ((int)threadIdx.x <= K + 1) so[threadIdx.x] = off[threadIdx.x];
   const int b = blockIdx.x * NWAVE + (threadIdx.x >> 6);
@@ -1295,7 +1304,9 @@ __global__ __launch_bounds__(WG) void k_lookup(const int32_t* keys, const int32_
     slot[b] = found;
   }
   for (int i = lane; i < K; i += 64)
-    toks[(int64_t)b * K + i] = found >= 0 ? payload[((int64_t)b * Bgt + found) * K + i] : -1;
+    toks[(int64_t)b * K + i] = found >= 0 ? payload[((int64_t)b * Bgt + found) * K + i]
+                               : fill     ? fallback_token(seed, b, i, V)
+                                          : -1;
 }
 
 // Keys of every (sequence, slot): slot sl of depth k (off[k] <= sl < off[k+1])

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <cmath>
 #include <vector>
 
 #include <hip/hip_ext.h>
@@ -288,6 +289,8 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
     if (!cache->fanout || !cache_layout(cache, K, V, p)) return SSD_ERR_INVALID_ARG;
     if (p.Bgt > 0 && !cache->keys) return SSD_ERR_INVALID_ARG;
     if (!cache->out_hit || !cache->out_slot || (K > 0 && !cache->out_tokens)) return SSD_ERR_INVALID_ARG;
+    if (cache->miss_fill != 0 && cache->miss_fill != 1) return SSD_ERR_INVALID_ARG;
+    p.fill = cache->miss_fill;
     if (K > 0 && p.Bgt > 0 && !cache->payload) return SSD_ERR_INVALID_ARG;
     p.ckeys = cache->keys;
     p.cpay = cache->payload;
@@ -336,15 +339,18 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
 
 ssd_status ssd_cache_lookup(const int32_t* keys, const int32_t* depth_off, const int32_t* payload, int32_t B,
                             int32_t K, int32_t Bgt, const int32_t* accept_len, const int32_t* bonus,
-                            int32_t* out_hit, int32_t* out_slot, int32_t* out_tokens, void* stream) {
+                            int32_t* out_hit, int32_t* out_slot, int32_t* out_tokens, int32_t miss_fill,
+                            int64_t V, uint64_t seed, void* stream) {
   if (B < 1 || K < 0 || K > SSD_MAX_K || Bgt < 0) return SSD_ERR_INVALID_ARG;
+  if (miss_fill != 0 && miss_fill != 1) return SSD_ERR_INVALID_ARG;
+  if (miss_fill && (V < 1 || V > SSD_MAX_V)) return SSD_ERR_INVALID_ARG;
   if (!depth_off || !accept_len || !bonus || !out_hit || !out_slot) return SSD_ERR_INVALID_ARG;
   if (Bgt > 0 && !keys) return SSD_ERR_INVALID_ARG;
   if (K > 0 && Bgt > 0 && !payload) return SSD_ERR_INVALID_ARG;
   if (K > 0 && !out_tokens) return SSD_ERR_INVALID_ARG;
   (void)hipGetLastError();
   k_lookup<<<dim3((unsigned)cdiv(B, NWAVE)), dim3(WG), 0, (hipStream_t)stream>>>(
-      keys, depth_off, payload, B, K, Bgt, accept_len, bonus, out_hit, out_slot, out_tokens);
+      keys, depth_off, payload, B, K, Bgt, accept_len, bonus, out_hit, out_slot, out_tokens, V, seed, miss_fill);
   return hip_status(hipGetLastError());
 }
 
@@ -437,6 +443,29 @@ ssd_status ssd_fanout(int32_t Bgt, int32_t K, double ratio, int64_t V, int32_t* 
     excess -= give;
   }
   for (int k = 0; k <= K; ++k) out_F[k] = (int32_t)F[k];
+  return SSD_OK;
+}
+
+ssd_status ssd_backoff(const double* p_hit, int32_t B, const ssd_backoff_cost* c, int32_t* out_use_fast,
+                       double* out_gain) {
+  if (!p_hit || !c || !out_use_fast || B < 1) return SSD_ERR_INVALID_ARG;
+  if (!(c->t_round > 0.0) || !(c->t_slow >= 0.0) || !(c->t_fast >= 0.0) || !(c->e_acc > 0.0) ||
+      !(c->e_fast >= 0.0) || !std::isfinite(c->t_round) || !std::isfinite(c->t_slow) || !std::isfinite(c->t_fast) ||
+      !std::isfinite(c->e_acc) || !std::isfinite(c->e_fast))
+    return SSD_ERR_INVALID_ARG;
+  double P = 1.0, mix = 0.0;
+  for (int32_t b = 0; b < B; ++b) {
+    const double p = p_hit[b];
+    if (!(p >= 0.0 && p <= 1.0)) return SSD_ERR_INVALID_ARG;
+    P *= p;
+    mix += p * c->e_acc + (1.0 - p) * c->e_fast;
+  }
+  // tokens per unit time with each backup; a round with any miss waits for it
+  const double r_acc = (double)B * c->e_acc / (c->t_round + (1.0 - P) * c->t_slow);
+  const double r_fast = mix / (c->t_round + (1.0 - P) * c->t_fast);
+  const double gain = r_fast / r_acc;
+  *out_use_fast = gain > 1.0 ? 1 : 0;
+  if (out_gain) *out_gain = gain;
   return SSD_OK;
 }
 

@@ -20,6 +20,9 @@ GPU side only as a written definition (no code is shared):
 * uniform u = ((word >> 9) + 0.5) * 2**-23, an odd multiple of 2**-24 in
   (0, 1) that is exactly representable in binary32 and binary64.
 * Gumbel  g = -ln(-ln u).
+* a random token in [0, V) from a word: floor(word * V / 2**32), the high
+  half of the 64-bit product (every token gets floor or ceil of 2**32 / V
+  words).
 """
 import numpy as np
 
@@ -35,6 +38,7 @@ DRAFT_BLOCK = 1
 ACCEPT = 2
 BONUS_TOKEN = 3
 BONUS_BLOCK = 4
+FALLBACK = 5  # random tokens that stand in for a missed cache entry
 
 
 def philox4x32_10(ctr, key):
@@ -91,3 +95,9 @@ def gumbel_from_uniform(u):
 
 def gumbels(seed, b, j, stream, idx):
     return gumbel_from_uniform(uniforms(seed, b, j, stream, idx))
+
+
+def token_from_word(w, V):
+    """floor(w * V / 2**32): a token in [0, V) from a 32-bit word."""
+    w = np.asarray(w, dtype=np.uint64)
+    return ((w * np.uint64(V)) >> np.uint64(32)).astype(np.int64)

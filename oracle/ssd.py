@@ -401,10 +401,23 @@ def build_keys(topf_idx, Fk):
     return keys, off
 
 
-def cache_lookup(keys, off, payload, accept_len, bonus):
+def fallback_tokens(seed, b, K, V):
+    """The K random tokens that stand in for sequence b's missed cache entry:
+    token i from the FALLBACK stream word at (idx = i, b, j = 0), mapped to
+    [0, V) by the high half of word * V.  [SSD-B] part 3: past a critical
+    batch size a miss is served by a near-zero-latency speculator such as
+    random tokens."""
+    if K == 0:
+        return np.zeros(0, np.int64)
+    w = ph.draw_words(seed, b, 0, ph.FALLBACK, np.arange(K))
+    return ph.token_from_word(w, V)
+
+
+def cache_lookup(keys, off, payload, accept_len, bonus, seed=0, V=0, miss_fill=False):
     """Hit iff bonus is among depth accept_len's keys; slot = the lowest
-    such; tokens = payload[slot] or -1 (slot -1) on a miss.  An accepted
-    length outside [0, K] is a miss."""
+    such; tokens = payload[slot].  On a miss slot = -1 and the tokens are -1,
+    or with miss_fill the sequence's fallback tokens.  An accepted length
+    outside [0, K] is a miss."""
     keys = np.asarray(keys)
     payload = np.asarray(payload)
     B = keys.shape[0]
@@ -414,12 +427,52 @@ def cache_lookup(keys, off, payload, accept_len, bonus):
     toks = np.full((B, K), -1, np.int64)
     for b in range(B):
         k = int(accept_len[b])
-        if not (0 <= k < len(off) - 1):
-            continue
-        for s in range(off[k], off[k + 1]):
-            if keys[b, s] == bonus[b]:
-                hit[b] = 1
-                slot[b] = s
-                toks[b] = payload[b, s]
-                break
+        if 0 <= k < len(off) - 1:
+            for s in range(off[k], off[k + 1]):
+                if keys[b, s] == bonus[b]:
+                    hit[b] = 1
+                    slot[b] = s
+                    toks[b] = payload[b, s]
+                    break
+        if not hit[b] and miss_fill:
+            toks[b] = fallback_tokens(seed, b, K, V)
     return hit, slot, toks
+
+
+def backoff(p_hit, t_round, t_slow, t_fast, e_acc, e_fast):
+    """Which backup speculator serves cache misses ([SSD-B] part 3, reading).
+
+    A round in which any sequence misses waits for the backup, so with the
+    chance that the whole batch hits P = prod_b p_b (the pages' observation
+    that misses grow with the batch size):
+      accurate backup: every sequence yields e_acc tokens, the round takes
+                       t_round + (1 - P) t_slow;
+      fast backup:     sequence b yields p_b e_acc + (1 - p_b) e_fast tokens,
+                       the round takes t_round + (1 - P) t_fast.
+    Returns (use_fast, gain) with gain = throughput(fast) / throughput(accurate);
+    the fast backup is chosen iff gain > 1 (a tie keeps the accurate one)."""
+    p = np.asarray(p_hit, dtype=np.float64)
+    B = p.size
+    P = float(np.prod(p))
+    r_acc = B * e_acc / (t_round + (1.0 - P) * t_slow)
+    r_fast = float(np.sum(p * e_acc + (1.0 - p) * e_fast)) / (t_round + (1.0 - P) * t_fast)
+    gain = r_fast / r_acc
+    return bool(gain > 1.0), gain
+
+
+def backoff_critical_batch(p, t_round, t_slow, t_fast, e_acc, e_fast):
+    """Smallest real batch size B* from which the fast backup wins when every
+    sequence hits with chance p (0 < p < 1): equal throughputs at a batch
+    miss chance q* = t_round (e_acc - e_mix) / (e_mix t_slow - e_acc t_fast),
+    e_mix = p e_acc + (1 - p) e_fast, and 1 - p**B* = q*.  inf when the fast
+    backup never wins."""
+    e_mix = p * e_acc + (1.0 - p) * e_fast
+    den = e_mix * t_slow - e_acc * t_fast
+    if den <= 0.0:
+        return float("inf")
+    q = t_round * (e_acc - e_mix) / den
+    if q >= 1.0:
+        return float("inf")
+    if q <= 0.0:
+        return 0.0
+    return float(np.log1p(-q) / np.log(p))

@@ -197,6 +197,16 @@ def test_cache_lookup_against_oracle():
     assert np.array_equal(slot.cpu().numpy(), os_)
     assert np.array_equal(toks.cpu().numpy(), ot)
     assert oh.sum() >= hits.numel() - 1
+    # misses filled with the random fallback tokens
+    seed = W.seed(cfg, 5)
+    hit, slot, toks = ssd.cache_lookup(keys, dev_off, payload, acc, bonus, miss_fill=True, V=cfg.V, seed=seed)
+    torch.cuda.synchronize()
+    oh, os_, ot = O.cache_lookup(ok_keys, off, payload.cpu().numpy(), acc.cpu().numpy(), bonus.cpu().numpy(),
+                                 seed=seed, V=cfg.V, miss_fill=True)
+    assert np.array_equal(hit.cpu().numpy(), oh)
+    assert np.array_equal(slot.cpu().numpy(), os_)
+    assert np.array_equal(toks.cpu().numpy(), ot)
+    assert (ot >= 0).all()
 
 
 def test_cache_keys_from_sampling_and_lookup_in_verify():
@@ -209,14 +219,16 @@ def test_cache_keys_from_sampling_and_lookup_in_verify():
     from oracle import ssd as O
     B, K, V = 8, 5, 128256
     cfg = W.custom(B, K, V, BF16, T=0.7, F=4, C=0.6, kind="peaks", draft_sd=0.8, F_out=4, Bgt=64, ratio=0.6)
-    Fk = ssd.fanout(64, K, 0.6, V)
-    for step in range(3):
-        _say(f"cache path step {step}")
+    for step in range(4):
+        # budgets up to 64 keep each sequence's keys in registers, larger ones read them
+        budget, fill = (64, 100)[step // 2], step % 2 == 1
+        Fk = ssd.fanout(budget, K, 0.6, V)
+        _say(f"cache path step {step}: budget {budget} fan-out {Fk} miss fill {fill}")
         t, d = W.logits(cfg, step, DEV)
         T = W.temperatures(cfg, DEV)
         seed = W.seed(cfg, step)
-        payload = W.payload(cfg, 64, step, DEV)
-        cache = ssd.Cache(Fk, B, K, DEV, payload=payload)
+        payload = W.payload(cfg, budget, step, DEV)
+        cache = ssd.Cache(Fk, B, K, DEV, payload=payload, miss_fill=fill)
         s1 = ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=4, cache=cache)
         s0 = ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=4)
         v1 = ssd.verify(t, d, T, cfg.F, cfg.C, seed, s1["tokens"], s1["q"], s1["stats"], s1["topf_idx"], cache=cache)
@@ -234,7 +246,7 @@ def test_cache_keys_from_sampling_and_lookup_in_verify():
         ok_keys, off = O.build_keys(lists, Fk)
         assert np.array_equal(cache.keys.cpu().numpy(), ok_keys)
         oh, os_, ot = O.cache_lookup(ok_keys, off, payload.cpu().numpy(), v1["accept_len"].cpu().numpy(),
-                                     v1["bonus"].cpu().numpy())
+                                     v1["bonus"].cpu().numpy(), seed=seed, V=V, miss_fill=fill)
         assert np.array_equal(cache.hit.cpu().numpy(), oh)
         assert np.array_equal(cache.slot.cpu().numpy(), os_)
         assert np.array_equal(cache.tokens.cpu().numpy(), ot)

@@ -18,7 +18,8 @@ def L():
     if not os.path.exists(ssd.LIB_PATH):
         from lossless_verify_sample_amd import build
         build.build(verbose=False)
-    return ssd.library()
+    ssd.library()  # loads libssd after the HIP runtime that torch brings
+    return ctypes.CDLL(ssd.LIB_PATH)  # own function objects: argtypes set here stay here
 
 
 def declared():
@@ -148,6 +149,34 @@ def test_entry_points_reject_invalid_arguments_on_host(L):
     tr.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert tr(9, P, P) == 1 and tr(2, N, P) == 1
     lk = L.ssd_cache_lookup
-    lk.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6
-    assert lk(P, N, P, 4, 3, 8, P, P, P, P, P, N) == 1   # no depth offsets
-    assert lk(P, P, P, 0, 3, 8, P, P, P, P, P, N) == 1   # B = 0
+    lk.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 5
+                   + [ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p])
+    assert lk(P, N, P, 4, 3, 8, P, P, P, P, P, 0, 0, 0, N) == 1   # no depth offsets
+    assert lk(P, P, P, 0, 3, 8, P, P, P, P, P, 0, 0, 0, N) == 1   # B = 0
+    assert lk(P, P, P, 4, 3, 8, P, P, P, P, P, 2, 100, 0, N) == 1  # miss_fill not 0/1
+    assert lk(P, P, P, 4, 3, 8, P, P, P, P, P, 1, 0, 0, N) == 1    # fill without a vocabulary
+
+
+def test_backoff_matches_oracle(L):
+    """The host back-off rule against the oracle's, on random hit rates,
+    batch sizes and costs: the same decision, the same gain to 1e-12."""
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        B = int(rng.integers(1, 600))
+        p = rng.uniform(0.3, 1.0, B) if rng.random() < 0.7 else np.full(B, rng.uniform(0.5, 1.0))
+        c = dict(t_round=rng.uniform(0.5, 2.0), t_slow=rng.uniform(0.0, 3.0), t_fast=rng.uniform(0.0, 0.2),
+                 e_acc=rng.uniform(1.0, 5.0), e_fast=rng.uniform(0.5, 1.5))
+        got = ssd.backoff(p, **c)
+        want = O.backoff(p, **c)
+        assert got[0] == want[0] and abs(got[1] - want[1]) <= 1e-12 * want[1], (B, c)
+
+
+def test_backoff_rejects_bad_arguments(L):
+    import lossless_verify_sample_amd as ssd
+    ok = dict(t_round=1.0, t_slow=1.0, t_fast=0.0, e_acc=2.0, e_fast=1.0)
+    for p, kw in (([], {}), ([1.5], {}), ([-0.1], {}), ([float("nan")], {}), ([0.5], {"t_round": 0.0}),
+                  ([0.5], {"t_slow": -1.0}), ([0.5], {"e_acc": 0.0}), ([0.5], {"e_fast": float("inf")})):
+        with pytest.raises(ssd.SSDError):
+            ssd.backoff(p, **dict(ok, **kw))
