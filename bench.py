@@ -134,11 +134,15 @@ def main():
     total = a.warmup + a.steps
     acc_buf = torch.zeros((total, B), dtype=torch.int32, device=dev)
     hit_buf = torch.zeros((total, B), dtype=torch.int32, device=dev)
-    smp_out = dict(tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
-                   q=torch.empty((B, K), dtype=torch.float32, device=dev),
-                   stats=torch.empty((cfg.rows, 2), dtype=torch.float64, device=dev),
-                   topf_idx=torch.empty((B, K + 1, Fo), dtype=torch.int32, device=dev),
-                   topf_val=torch.empty((B, K + 1, Fo), dtype=torch.float32, device=dev))
+    def smp_buffers():
+        return dict(tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
+                    q=torch.empty((B, K), dtype=torch.float32, device=dev),
+                    stats=torch.empty((cfg.rows, 2), dtype=torch.float64, device=dev),
+                    topf_idx=torch.empty((B, K + 1, Fo), dtype=torch.int32, device=dev),
+                    topf_val=torch.empty((B, K + 1, Fo), dtype=torch.float32, device=dev))
+
+    smp_bufs = [smp_buffers(), smp_buffers()]  # the sampling of step i + 1 beside step i's verification
+    smp_out = smp_bufs[0]
     bonus = torch.empty(B, dtype=torch.int32, device=dev)
     pout = torch.empty((B, K), dtype=torch.float32, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total)]
@@ -161,15 +165,51 @@ def main():
         if e:
             e[2].record()
 
+    # Headline schedule (ssd_round): step i's verification shares launches
+    # with step i + 1's sampling, as the draft speculates the next round
+    # while the target verifies in SSD; every step still does one full
+    # sampling and one full verification of its own inputs.
+    def sample_args(i):
+        return dict(draft=sets[i % nsets][1], temperature=T, F=cfg.F, C=cfg.C, seed=W.seed(cfg, i), F_out=Fo,
+                    out=smp_bufs[i % 2], cache=caches[i % nsets] if use_cache else None)
+
+    def verify_args(i):
+        t, d = sets[i % nsets]
+        smp = smp_bufs[i % 2]
+        cache = caches[i % nsets] if use_cache else None
+        if cache is not None:
+            cache.hit = hit_buf[i]
+        return dict(target=t, draft=d, temperature=T, F=cfg.F, C=cfg.C, seed=W.seed(cfg, i), tokens=smp["tokens"],
+                    draft_q=smp["q"], draft_stats=smp["stats"], draft_topf_idx=smp["topf_idx"],
+                    out=dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None), cache=cache)
+
+    def run_rounds(lo, hi):
+        ssd.round_step(None, sample_args(lo))
+        for i in range(lo, hi):
+            ssd.round_step(verify_args(i), sample_args(i + 1) if i + 1 < hi else None)
+
+    # the same steps with separate calls (sample, then verify)
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
     for i in range(a.warmup, total):
         step(i)
+    s1.record()
+    torch.cuda.synchronize()
+    acc_sep = acc_buf[a.warmup:].clone()
+    hit_sep = hit_buf[a.warmup:].clone()
+    run_rounds(0, a.warmup)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    run_rounds(a.warmup, total)
     stop.record()
     torch.cuda.synchronize()
+    same = bool(torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:]))
+    if not same:
+        raise SystemExit("ssd_round gave other accepted lengths or cache hits than the separate calls")
     # instrumented pass: the same steps again with per-call events and the
     # streaming launches stamped by their own events (kept out of the headline
     # pass, whose step time the event work would inflate)
@@ -180,6 +220,7 @@ def main():
     k_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
     ssd.timer_enable(0)
     ms = start.elapsed_time(stop) / a.steps
+    ms_sep = s0.elapsed_time(s1) / a.steps
     timed = range(a.warmup, total)
     t_s = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed) / a.steps
     t_v = sum(ev[i][1].elapsed_time(ev[i][2]) for i in timed) / a.steps
@@ -240,6 +281,8 @@ def main():
                                   if use_cache else ""),
                    "B": B, "K": K, "V": V, "input_sets": nsets, "input_gib": round(nsets * set_bytes / 2 ** 30, 2)},
         "tokens_per_s": round(tokens / (a.steps * ms * 1e-3), 1),
+        "schedule": "ssd_round: step i's verification shares launches with step i+1's sampling",
+        "ms_per_step_separate_calls": round(ms_sep, 5),
         "mean_accepted": round(float(acc.float().mean().item()), 4),
         "ms_sample": round(t_s, 5),
         "ms_verify": round(t_v, 5),

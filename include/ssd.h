@@ -215,6 +215,68 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
                       int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, const ssd_cache* cache,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/* The arguments of ssd_saguaro_sample and ssd_verify as structs, in the same
+ * order and with the same meaning (see those calls), for ssd_round. */
+typedef struct {
+  const void* draft_logits;
+  ssd_dtype dt;
+  int32_t B, K;
+  int64_t V, ld;
+  const float* temperature;
+  int32_t F;
+  float C;
+  int32_t F_out;
+  uint64_t seed;
+  int32_t* out_tokens;
+  float* out_q;
+  ssd_row_stats* out_stats;
+  int32_t* out_topf_idx;
+  float* out_topf_val;
+  const ssd_cache* cache;
+  void* workspace;
+  size_t ws_bytes;
+} ssd_sample_args;
+
+typedef struct {
+  const void* target_logits;
+  const void* draft_logits;
+  ssd_dtype dt;
+  int32_t B, K;
+  int64_t V, ld;
+  const float* temperature;
+  int32_t F;
+  float C;
+  uint64_t seed;
+  const int32_t* draft_tokens;
+  const float* draft_q;
+  const ssd_row_stats* draft_stats;
+  const int32_t* draft_topf_idx;
+  int32_t ld_topf;
+  int32_t* out_accept_len;
+  int32_t* out_bonus;
+  float* out_p;
+  ssd_row_stats* out_target_stats;
+  const ssd_cache* cache;
+  void* workspace;
+  size_t ws_bytes;
+} ssd_verify_args;
+
+/* One step of the SSD pipeline ([SSD-A] and [SSD-B] core mechanism: the draft
+ * speculates the next round while the target verifies the current one):
+ * verification of round i (`v`) and draft sampling of round i+1 (`s`), with
+ * results identical to ssd_verify(v) followed by ssd_saguaro_sample(s).  The
+ * sampling does not depend on the verification, so the library pairs each
+ * latency-bound kernel of the verification with a kernel of the sampling in
+ * one launch (acceptance and residual pass beside sampling's streaming pass;
+ * bonus and cache lookup beside sampling's epilogue).  Either pointer may be
+ * NULL (then this is the other call alone).  The two calls need separate
+ * workspaces (SSD_ERR_WORKSPACE otherwise), and the sampling's outputs and
+ * cache keys must not be the verification's inputs or outputs (round i+1's
+ * buffers are not round i's).  When the element types or the 16-byte
+ * alignment of the two differ, the calls run one after the other.
+ * Errors: as the two calls. */
+ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream);
+
 /* Speculation-cache lookup keyed by (accepted length, bonus token) ([SSD-B]
  * core-mechanism section: the draft builds a speculation cache while the
  * target verifies and a single lookup follows; [SSD-A]: on a hit the prepared

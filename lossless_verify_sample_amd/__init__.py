@@ -14,7 +14,7 @@ import os
 import torch  # provides the process's HIP runtime, which libssd then shares
 
 __all__ = [
-    "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "cache_keys", "cache_lookup",
+    "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "round_step", "cache_keys", "cache_lookup",
     "fanout", "backoff", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
 ]
 
@@ -35,6 +35,21 @@ class SSDError(RuntimeError):
 class _CacheStruct(ctypes.Structure):
     _fields_ = [("fanout", _vp), ("keys", _vp), ("payload", _vp), ("out_hit", _vp), ("out_slot", _vp),
                 ("out_tokens", _vp), ("miss_fill", ctypes.c_int32)]
+
+
+class _SampleArgs(ctypes.Structure):  # ssd_sample_args
+    _fields_ = [("draft_logits", _vp), ("dt", ctypes.c_int), ("B", _i32), ("K", _i32), ("V", _i64), ("ld", _i64),
+                ("temperature", _vp), ("F", _i32), ("C", _f32), ("F_out", _i32), ("seed", _u64),
+                ("out_tokens", _vp), ("out_q", _vp), ("out_stats", _vp), ("out_topf_idx", _vp),
+                ("out_topf_val", _vp), ("cache", _vp), ("workspace", _vp), ("ws_bytes", _sz)]
+
+
+class _VerifyArgs(ctypes.Structure):  # ssd_verify_args
+    _fields_ = [("target_logits", _vp), ("draft_logits", _vp), ("dt", ctypes.c_int), ("B", _i32), ("K", _i32),
+                ("V", _i64), ("ld", _i64), ("temperature", _vp), ("F", _i32), ("C", _f32), ("seed", _u64),
+                ("draft_tokens", _vp), ("draft_q", _vp), ("draft_stats", _vp), ("draft_topf_idx", _vp),
+                ("ld_topf", _i32), ("out_accept_len", _vp), ("out_bonus", _vp), ("out_p", _vp),
+                ("out_target_stats", _vp), ("cache", _vp), ("workspace", _vp), ("ws_bytes", _sz)]
 
 
 class _BackoffCost(ctypes.Structure):
@@ -100,6 +115,7 @@ def _load():
                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
         "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _u64, _vp],
         "ssd_backoff": [_vp, _i32, _vp, _vp, _vp],
+        "ssd_round": [_vp, _vp, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
     }
@@ -249,7 +265,7 @@ def topf(logits, F):
     return idx, val
 
 
-def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=None):
+def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=None, _defer=None):
     """Draft sampling with sigma_{F,C} over draft logits [B, K+1, V].
 
     Returns dict(tokens [B,K] int32, q [B,K] f32, stats [B*(K+1), 2] (see
@@ -271,17 +287,19 @@ def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=N
                    topf_idx=torch.empty((B, K1, F_out), dtype=torch.int32, device=dev),
                    topf_val=torch.empty((B, K1, F_out), dtype=torch.float32, device=dev))
     ws = _workspace(OP_SAMPLE, B, K, V, dev)
-    _check(_lib.ssd_saguaro_sample(_p(draft), _DT[draft.dtype], B, K, V, ld, _p(temperature), F, float(C), F_out,
-                                   int(seed) & (2 ** 64 - 1), _p(out["tokens"]), _p(out["q"]), _p(out["stats"]),
-                                   _p(out["topf_idx"]), _p(out["topf_val"]),
-                                   ctypes.byref(cache._struct(dev, False)) if cache is not None else None,
-                                   _p(ws), ws.numel(), _stream(dev)),
-           "ssd_saguaro_sample")
+    cs = cache._struct(dev, False) if cache is not None else None
+    args = (_p(draft), _DT[draft.dtype], B, K, V, ld, _p(temperature), F, float(C), F_out, int(seed) & (2 ** 64 - 1),
+            _p(out["tokens"]), _p(out["q"]), _p(out["stats"]), _p(out["topf_idx"]), _p(out["topf_val"]),
+            ctypes.cast(ctypes.pointer(cs), _vp) if cs is not None else None, _p(ws), ws.numel())
+    if _defer is not None:
+        _defer.extend([cs])
+        return out, args
+    _check(_lib.ssd_saguaro_sample(*args, _stream(dev)), "ssd_saguaro_sample")
     return out
 
 
 def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats, draft_topf_idx, want_stats=False,
-           out=None, cache=None):
+           out=None, cache=None, _defer=None):
     """Acceptance test, accepted length and bonus for target/draft [B, K+1, V].
 
     Returns dict(accept_len [B] int32, bonus [B] int32, p [B,K] f32, stats
@@ -307,13 +325,41 @@ def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats,
                    p=torch.empty((B, K), dtype=torch.float32, device=dev),
                    stats=_stats_tensor(B * K1, dev) if want_stats else None)
     ws = _workspace(OP_VERIFY, B, K, V, dev)
-    _check(_lib.ssd_verify(_p(target), _p(draft), _DT[target.dtype], B, K, V, ld, _p(temperature), F, float(C),
-                           int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_q), _p(draft_stats),
-                           _p(draft_topf_idx) if F > 0 else None, ldf, _p(out["accept_len"]), _p(out["bonus"]),
-                           _p(out["p"]), _p(out.get("stats")),
-                           ctypes.byref(cache._struct(dev, True)) if cache is not None else None,
-                           _p(ws), ws.numel(), _stream(dev)), "ssd_verify")
+    cs = cache._struct(dev, True) if cache is not None else None
+    args = (_p(target), _p(draft), _DT[target.dtype], B, K, V, ld, _p(temperature), F, float(C),
+            int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_q), _p(draft_stats),
+            _p(draft_topf_idx) if F > 0 else None, ldf, _p(out["accept_len"]), _p(out["bonus"]),
+            _p(out["p"]), _p(out.get("stats")), ctypes.cast(ctypes.pointer(cs), _vp) if cs is not None else None,
+            _p(ws), ws.numel())
+    if _defer is not None:
+        _defer.extend([cs])
+        return out, args
+    _check(_lib.ssd_verify(*args, _stream(dev)), "ssd_verify")
     return out
+
+
+def round_step(verify_args=None, sample_args=None):
+    """One pipeline step (ssd_round): verification of round i and draft
+    sampling of round i + 1, each given as a dict of the keyword arguments of
+    verify() / saguaro_sample() (with their positional ones under the same
+    names).  Results are those of verify(...) then saguaro_sample(...); the
+    sampling's outputs must not be the verification's inputs.  Returns
+    (verify outputs or None, sample outputs or None)."""
+    keep = []
+    vo = so = None
+    vs = ss = None
+    if verify_args is not None:
+        vo, a = verify(**verify_args, _defer=keep)
+        vs = _VerifyArgs(*a)
+    if sample_args is not None:
+        so, a = saguaro_sample(**sample_args, _defer=keep)
+        ss = _SampleArgs(*a)
+    if vs is None and ss is None:
+        raise SSDError("round_step needs a verification or a sampling")
+    dev = (verify_args["target"] if verify_args is not None else sample_args["draft"]).device
+    _check(_lib.ssd_round(ctypes.byref(vs) if vs is not None else None, ctypes.byref(ss) if ss is not None else None,
+                          _stream(dev)), "ssd_round")
+    return vo, so
 
 
 def cache_keys(topf_idx, depth_off, Bgt):

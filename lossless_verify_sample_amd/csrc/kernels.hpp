@@ -54,6 +54,7 @@ struct Params {
   int64_t V, ld;            // ld in elements
   int64_t rows;             // rows streamed by the kernel
   int NB, nchunk;           // blocks per row, workgroups per row
+  int racc;                 // verification: blocks per workgroup of the residual pass (a multiple of CH_R)
   int K, B;
   const float* temp;
   int F, F_out, F_sel;
@@ -927,25 +928,12 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     if (tid == 0) p.bonus[b] = x >= 0 ? x : 0;
     return;
   }
-  // residual block sums of this chunk's blocks (two per wave, all loads in flight together)
-  const int be0 = chunk * CH_R + wave, be1 = be0 + ENW;
-  if (be0 >= NB) return;
+  // residual block sums of this chunk's blocks, CH_R at a time (two per
+  // wave, all their loads in flight together)
   const SeqState ss = sm.ss;
   const int64_t row = r0 + ks;
   const unsigned char* rt = p.x + row * rs;
   const unsigned char* rd = p.xd + row * rs;
-  RawBlock<DT, AL> ut0, ud0, ut1, ud1;
-  if ((chunk + 1) * CH_R * BLK <= V) {
-    load_raw<DT, AL, true>(rt, V, be0, lane, ut0);
-    load_raw<DT, AL, true>(rd, V, be0, lane, ud0);
-    load_raw<DT, AL, true>(rt, V, be1, lane, ut1);
-    load_raw<DT, AL, true>(rd, V, be1, lane, ud1);
-  } else {
-    load_raw<DT, AL, false>(rt, V, be0, lane, ut0);
-    load_raw<DT, AL, false>(rd, V, be0, lane, ud0);
-    load_raw<DT, AL, false>(rt, V, min(be1, NB - 1), lane, ut1);
-    load_raw<DT, AL, false>(rd, V, min(be1, NB - 1), lane, ud1);
-  }
   const float ot = ss.o_t, od = ss.o_d, nk = -ss.kf;
   const int64_t rrow = row * p.ld_dtopf;
   auto residual = [&](const RawBlock<DT, AL>& ut, const RawBlock<DT, AL>& ud, int be) {
@@ -989,8 +977,25 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     }
     if (lane == 0) p.rpart[(int64_t)b * NB + be] = make_float2(fmaxf(R, 0.f), Mt);
   };
-  residual(ut0, ud0, be0);
-  if (be1 < NB) residual(ut1, ud1, be1);
+  const int end = min(NB, (chunk + 1) * p.racc);
+  for (int base = chunk * p.racc; base < end; base += CH_R) {
+    const int be0 = base + wave, be1 = be0 + ENW;
+    if (be0 >= end) break;
+    RawBlock<DT, AL> ut0, ud0, ut1, ud1;
+    if ((base + CH_R) * BLK <= V) {
+      load_raw<DT, AL, true>(rt, V, be0, lane, ut0);
+      load_raw<DT, AL, true>(rd, V, be0, lane, ud0);
+      load_raw<DT, AL, true>(rt, V, be1, lane, ut1);
+      load_raw<DT, AL, true>(rd, V, be1, lane, ud1);
+    } else {
+      load_raw<DT, AL, false>(rt, V, be0, lane, ut0);
+      load_raw<DT, AL, false>(rd, V, be0, lane, ud0);
+      load_raw<DT, AL, false>(rt, V, min(be1, NB - 1), lane, ut1);
+      load_raw<DT, AL, false>(rd, V, min(be1, NB - 1), lane, ud1);
+    }
+    residual(ut0, ud0, be0);
+    if (be1 < end) residual(ut1, ud1, be1);
+  }
 }
 
 template <int DT, bool AL>
@@ -1059,8 +1064,7 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
 // ---------------------------------------------------------------------------
 // (f32 and unaligned rows need more registers per element: fewer waves)
 template <int DT, bool AL, int MODE>
-__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(Params p) {
-  const int item = blockIdx.x;
+__device__ __forceinline__ void stream_item(const Params& p, int item) {
   const int64_t row = item / p.nchunk;
   const int chunk = item - (int)(row * p.nchunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1105,6 +1109,19 @@ __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(P
   }
 }
 
+template <int DT, bool AL, int MODE>
+__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(Params p) {
+  stream_item<DT, AL, MODE>(p, blockIdx.x);
+}
+
+// Sampling epilogue item g: row g, or (g >= rows) a long cache-key list.
+template <int DT, bool AL>
+__device__ __forceinline__ void sample_epi_item(const Params& p, int g, ESm& sm) {
+  const bool small = p.NB <= 128;
+  if (g < p.rows) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
+  else small ? epi_keys_p<DT, AL, 2>(p, g - (int)p.rows, sm) : epi_keys_p<DT, AL, NBL>(p, g - (int)p.rows, sm);
+}
+
 // One workgroup per row (per sequence for verification) over the partials.
 template <int DT, bool AL, int MODE>
 __global__ __launch_bounds__(EWG) void k_epi(Params p) {
@@ -1114,19 +1131,21 @@ __global__ __launch_bounds__(EWG) void k_epi(Params p) {
   const bool small = p.NB <= 128;
   if constexpr (MODE == M_SOFTMAX) small ? epi_softmax_p<DT, AL, 2>(p, g) : epi_softmax_p<DT, AL, NBL>(p, g);
   if constexpr (MODE == M_TOPF) small ? epi_topf_p<DT, AL, 2>(p, g, sm) : epi_topf_p<DT, AL, NBL>(p, g, sm);
-  if constexpr (MODE == M_SAMPLE) {
-    if (g < p.rows) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
-    else small ? epi_keys_p<DT, AL, 2>(p, g - (int)p.rows, sm) : epi_keys_p<DT, AL, NBL>(p, g - (int)p.rows, sm);
-  }
+  if constexpr (MODE == M_SAMPLE) sample_epi_item<DT, AL>(p, g, sm);
 }
 
 // Acceptance and residual pass (one workgroup per sequence and chunk).
 template <int DT, bool AL>
-__global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(Params p) {
-  __shared__ ESm sm;
-  const int b = blockIdx.x / p.nchunk, chunk = blockIdx.x - b * p.nchunk;
+__device__ __forceinline__ void accept_item(const Params& p, int item, ESm& sm) {
+  const int b = item / p.nchunk, chunk = item - b * p.nchunk;
   if (p.NB <= 128) accept_residual<DT, AL, 2>(p, b, chunk, sm);
   else accept_residual<DT, AL, NBL>(p, b, chunk, sm);
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(Params p) {
+  __shared__ ESm sm;
+  accept_item<DT, AL>(p, blockIdx.x, sm);
 }
 
 // Wave 0's copy of sequence b's keys and payload, one slot per lane, when
@@ -1205,9 +1224,8 @@ __device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k,
 // Bonus from the residual for the sequences that need it, then (when asked)
 // the cache lookup of every sequence's (k*, bonus).
 template <int DT, bool AL>
-__global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
-  __shared__ ESm sm;
-  const int b = blockIdx.x, NB = p.NB;
+__device__ __forceinline__ void residual_item(const Params& p, int b, ESm& sm) {
+  const int NB = p.NB;
   // the residual sums (used only when the state asks for them), the state,
   // and the outcome of sequences decided earlier are loaded together
   float R[NBT], Mt[NBT];
@@ -1235,6 +1253,31 @@ __global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
   } else if (threadIdx.x < 64) {
     cache_lookup_wave(p, b, ks0, y0, cr);
   }
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
+  __shared__ ESm sm;
+  residual_item<DT, AL>(p, blockIdx.x, sm);
+}
+
+// One round of the pipeline in two launches that each pair a latency-bound
+// kernel of verification (round i) with a kernel of sampling (round i + 1),
+// which does not depend on it: workgroups below nv take the verification
+// role.  (1) acceptance and residual pass beside sampling's streaming pass;
+// (2) bonus and cache lookup beside sampling's epilogue.
+template <int DT, bool AL>
+__global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_round_mid(Params pv, Params ps, int nv) {
+  __shared__ ESm sm;
+  if ((int)blockIdx.x < nv) accept_item<DT, AL>(pv, blockIdx.x, sm);
+  else stream_item<DT, AL, M_SAMPLE>(ps, (int)blockIdx.x - nv);
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(EWG) void k_round_tail(Params pv, Params ps, int nv) {
+  __shared__ ESm sm;
+  if ((int)blockIdx.x < nv) residual_item<DT, AL>(pv, blockIdx.x, sm);
+  else sample_epi_item<DT, AL>(ps, (int)blockIdx.x - nv, sm);
 }
 
 // Dense probabilities for ssd_softmax_t (after the statistics kernel).

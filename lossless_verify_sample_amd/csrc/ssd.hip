@@ -90,6 +90,18 @@ SSD_LAUNCHER_E(LAccept, (k_accept<DT, AL>))
 SSD_LAUNCHER_E(LResidualEpi, (k_residual_epi<DT, AL>))
 SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
 
+// A launch of two parameter sets (verification's kernel beside sampling's).
+#define SSD_LAUNCHER2(NAME, KERNEL)                                                          \
+  template <int DT, bool AL>                                                              \
+  struct NAME {                                                                           \
+    static hipError_t go(int64_t grid, const Params& pv, const Params& ps, int nv, hipStream_t st) { \
+      KERNEL<<<dim3((unsigned)grid), dim3(EWG), 0, st>>>(pv, ps, nv);                     \
+      return hipGetLastError();                                                           \
+    }                                                                                     \
+  };
+SSD_LAUNCHER2(LRoundMid, (k_round_mid<DT, AL>))
+SSD_LAUNCHER2(LRoundTail, (k_round_tail<DT, AL>))
+
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
 bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
@@ -97,6 +109,7 @@ bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
 }
 
 const int64_t kMaxGrid = 0x7fffffff;
+constexpr int RACC_ROUND = 5;  // residual blocks per workgroup in ssd_round, in units of CH_R
 
 // Depth offsets of a cache descriptor into p (false for a bad fan-out).
 bool cache_layout(const ssd_cache* c, int K, int64_t V, Params& p) {
@@ -140,6 +153,147 @@ hipError_t timed(ssd_op op, F launch) {
     return e;
   }
   return launch(nullptr, nullptr);
+}
+
+// A checked call: kernel parameters, element type, alignment, grid sizes.
+struct Plan {
+  Params p{};
+  int dt = 0;
+  bool al = false;
+  int64_t g_stream = 0;  // streaming pass
+  int64_t g_accept = 0;  // verification: acceptance and residual pass
+  int nch_accept = 0;
+  int64_t g_tail = 0;    // sampling epilogue / verification bonus kernel
+};
+
+ssd_status plan_sample(const ssd_sample_args& a, Plan& q) {
+  const int32_t B = a.B, K = a.K, F = a.F, F_out = a.F_out;
+  const int64_t V = a.V, ld = a.ld;
+  const float C = a.C;
+  if (!a.draft_logits || !a.temperature || !a.out_stats || !dt_ok(a.dt)) return SSD_ERR_INVALID_ARG;
+  if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
+  if (K > 0 && (!a.out_tokens || !a.out_q)) return SSD_ERR_INVALID_ARG;
+  if (F < 0 || F > SSD_MAX_F || F > V || F_out < F || F_out > SSD_MAX_F || F_out > V) return SSD_ERR_INVALID_ARG;
+  if (F_out > 0 && !a.out_topf_idx && !a.out_topf_val) return SSD_ERR_INVALID_ARG;
+  if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
+  Params& p = q.p;
+  p = Params{};
+  const ssd_cache* cache = a.cache;
+  if (cache) {
+    if (!cache->fanout || !cache->keys || !cache_layout(cache, K, V, p)) return SSD_ERR_INVALID_ARG;
+    p.ckeys = cache->keys;
+  }
+  Layout L;
+  if (!layout(SSD_OP_SAMPLE, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
+  if (!ws_ok(a.workspace, a.ws_bytes, L)) return SSD_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * (K + 1);
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
+  if (rows * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  p.x = (const unsigned char*)a.draft_logits;
+  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
+  p.K = K; p.B = B;
+  p.temp = a.temperature;
+  p.F = F; p.F_out = F_out; p.F_sel = F_out > 1 ? F_out : 1;
+  if (cache) {
+    for (int j = 0; j <= K; ++j)
+      if (cache->fanout[j] > p.F_sel) p.kdep[p.nkd++] = j;
+  }
+  p.C = C; p.seed = a.seed;
+  char* ws = (char*)a.workspace;
+  p.part = (float4*)(ws + L.part);
+  p.stats = a.out_stats;
+  p.out_idx = F_out > 0 ? a.out_topf_idx : nullptr;
+  p.out_val = F_out > 0 ? a.out_topf_val : nullptr;
+  p.tokens = a.out_tokens;
+  p.q = a.out_q;
+  q.dt = a.dt;
+  q.al = aligned16(a.draft_logits, ld, V, a.dt);
+  q.g_stream = rows * nch;
+  q.g_tail = rows + (int64_t)p.nkd * B;
+  return SSD_OK;
+}
+
+hipError_t launch_sample(const Plan& q, hipStream_t st) {
+  hipError_t e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
+    return dispatch<LSample>(q.dt, q.al, q.g_stream, q.p, st, e0, e1);
+  });
+  if (e == hipSuccess) e = dispatch<LSampleEpi>(q.dt, q.al, q.g_tail, q.p, st);
+  return e;
+}
+
+ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
+  const int32_t B = a.B, K = a.K, F = a.F;
+  const int64_t V = a.V, ld = a.ld;
+  const float C = a.C;
+  if (!a.target_logits || !a.draft_logits || !a.temperature || !dt_ok(a.dt)) return SSD_ERR_INVALID_ARG;
+  if (!a.draft_stats || !a.out_accept_len || !a.out_bonus) return SSD_ERR_INVALID_ARG;
+  if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
+  if (K > 0 && (!a.draft_tokens || !a.draft_q || !a.out_p)) return SSD_ERR_INVALID_ARG;
+  if (F < 0 || F > SSD_MAX_F || F > V) return SSD_ERR_INVALID_ARG;
+  if (F > 0 && (!a.draft_topf_idx || a.ld_topf < F)) return SSD_ERR_INVALID_ARG;
+  if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
+  Params& p = q.p;
+  p = Params{};
+  const ssd_cache* cache = a.cache;
+  if (cache) {
+    if (!cache->fanout || !cache_layout(cache, K, V, p)) return SSD_ERR_INVALID_ARG;
+    if (p.Bgt > 0 && !cache->keys) return SSD_ERR_INVALID_ARG;
+    if (!cache->out_hit || !cache->out_slot || (K > 0 && !cache->out_tokens)) return SSD_ERR_INVALID_ARG;
+    if (cache->miss_fill != 0 && cache->miss_fill != 1) return SSD_ERR_INVALID_ARG;
+    p.fill = cache->miss_fill;
+    if (K > 0 && p.Bgt > 0 && !cache->payload) return SSD_ERR_INVALID_ARG;
+    p.ckeys = cache->keys;
+    p.cpay = cache->payload;
+    p.chit = cache->out_hit;
+    p.cslot = cache->out_slot;
+    p.ctok = cache->out_tokens;
+    p.lookup = 1;
+  }
+  Layout L;
+  if (!layout(SSD_OP_VERIFY, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
+  if (!ws_ok(a.workspace, a.ws_bytes, L)) return SSD_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * (K + 1);
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH), nchr = cdiv(NB, CH_R);
+  if (rows * nch > kMaxGrid || (int64_t)B * nchr > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  p.x = (const unsigned char*)a.target_logits;
+  p.xd = (const unsigned char*)a.draft_logits;
+  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
+  p.K = K; p.B = B;
+  p.temp = a.temperature;
+  p.F = F; p.C = C; p.seed = a.seed;
+  char* ws = (char*)a.workspace;
+  p.part = (float4*)(ws + L.part);
+  p.state = (SeqState*)(ws + L.state);
+  p.rpart = (float2*)(ws + L.rpart);
+  p.stats = a.out_target_stats;
+  p.dtok = a.draft_tokens;
+  p.dq = a.draft_q;
+  p.zcap = (float*)(ws + L.zcap);
+  p.dstats = a.draft_stats;
+  p.dtopf = F > 0 ? a.draft_topf_idx : nullptr;
+  p.ld_dtopf = a.ld_topf;
+  p.acc_len = a.out_accept_len;
+  p.bonus = a.out_bonus;
+  p.p_out = a.out_p;
+  q.dt = a.dt;
+  q.al = aligned16(a.target_logits, ld, V, a.dt) && aligned16(a.draft_logits, ld, V, a.dt);
+  q.g_stream = rows * nch;
+  q.g_accept = (int64_t)B * nchr;
+  q.nch_accept = (int)nchr;
+  p.racc = CH_R;
+  q.g_tail = B;
+  return SSD_OK;
+}
+
+hipError_t launch_verify(const Plan& q, hipStream_t st) {
+  Params p = q.p;
+  hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
+    return dispatch<LVerify>(q.dt, q.al, q.g_stream, p, st, e0, e1);
+  });
+  p.nchunk = q.nch_accept;
+  if (e == hipSuccess) e = dispatch<LAccept>(q.dt, q.al, q.g_accept, p, st);
+  if (e == hipSuccess) e = dispatch<LResidualEpi>(q.dt, q.al, q.g_tail, p, st);
+  return e;
 }
 
 }  // namespace
@@ -227,48 +381,13 @@ ssd_status ssd_saguaro_sample(const void* draft_logits, ssd_dtype dt, int32_t B,
                               uint64_t seed, int32_t* out_tokens, float* out_q, ssd_row_stats* out_stats,
                               int32_t* out_topf_idx, float* out_topf_val, const ssd_cache* cache,
                               void* workspace, size_t ws_bytes, void* stream) {
-  if (!draft_logits || !temperature || !out_stats || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
-  if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
-  if (K > 0 && (!out_tokens || !out_q)) return SSD_ERR_INVALID_ARG;
-  if (F < 0 || F > SSD_MAX_F || F > V || F_out < F || F_out > SSD_MAX_F || F_out > V) return SSD_ERR_INVALID_ARG;
-  if (F_out > 0 && !out_topf_idx && !out_topf_val) return SSD_ERR_INVALID_ARG;
-  if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
-  Params p{};
-  if (cache) {
-    if (!cache->fanout || !cache->keys || !cache_layout(cache, K, V, p)) return SSD_ERR_INVALID_ARG;
-    p.ckeys = cache->keys;
-  }
-  Layout L;
-  if (!layout(SSD_OP_SAMPLE, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
-  if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
-  const int64_t rows = (int64_t)B * (K + 1);
-  const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
-  if (rows * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
-  p.x = (const unsigned char*)draft_logits;
-  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
-  p.K = K; p.B = B;
-  p.temp = temperature;
-  p.F = F; p.F_out = F_out; p.F_sel = F_out > 1 ? F_out : 1;
-  if (cache) {
-    for (int j = 0; j <= K; ++j)
-      if (cache->fanout[j] > p.F_sel) p.kdep[p.nkd++] = j;
-  }
-  p.C = C; p.seed = seed;
-  char* ws = (char*)workspace;
-  p.part = (float4*)(ws + L.part);
-  p.stats = out_stats;
-  p.out_idx = F_out > 0 ? out_topf_idx : nullptr;
-  p.out_val = F_out > 0 ? out_topf_val : nullptr;
-  p.tokens = out_tokens;
-  p.q = out_q;
-  const bool al = aligned16(draft_logits, ld, V, dt);
+  const ssd_sample_args a{draft_logits, dt, B, K, V, ld, temperature, F, C, F_out, seed, out_tokens, out_q,
+                          out_stats, out_topf_idx, out_topf_val, cache, workspace, ws_bytes};
+  Plan q;
+  const ssd_status s = plan_sample(a, q);
+  if (s != SSD_OK) return s;
   (void)hipGetLastError();
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
-    return dispatch<LSample>(dt, al, rows * nch, p, st, e0, e1);
-  });
-  if (e == hipSuccess) e = dispatch<LSampleEpi>(dt, al, rows + (int64_t)p.nkd * B, p, st);
-  return hip_status(e);
+  return hip_status(launch_sample(q, (hipStream_t)stream));
 }
 
 ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_dtype dt, int32_t B, int32_t K,
@@ -277,63 +396,52 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
                       const int32_t* draft_topf_idx, int32_t ld_topf, int32_t* out_accept_len,
                       int32_t* out_bonus, float* out_p, ssd_row_stats* out_target_stats, const ssd_cache* cache,
                       void* workspace, size_t ws_bytes, void* stream) {
-  if (!target_logits || !draft_logits || !temperature || !dt_ok(dt)) return SSD_ERR_INVALID_ARG;
-  if (!draft_stats || !out_accept_len || !out_bonus) return SSD_ERR_INVALID_ARG;
-  if (B < 1 || K < 0 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
-  if (K > 0 && (!draft_tokens || !draft_q || !out_p)) return SSD_ERR_INVALID_ARG;
-  if (F < 0 || F > SSD_MAX_F || F > V) return SSD_ERR_INVALID_ARG;
-  if (F > 0 && (!draft_topf_idx || ld_topf < F)) return SSD_ERR_INVALID_ARG;
-  if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
-  Params p{};
-  if (cache) {
-    if (!cache->fanout || !cache_layout(cache, K, V, p)) return SSD_ERR_INVALID_ARG;
-    if (p.Bgt > 0 && !cache->keys) return SSD_ERR_INVALID_ARG;
-    if (!cache->out_hit || !cache->out_slot || (K > 0 && !cache->out_tokens)) return SSD_ERR_INVALID_ARG;
-    if (cache->miss_fill != 0 && cache->miss_fill != 1) return SSD_ERR_INVALID_ARG;
-    p.fill = cache->miss_fill;
-    if (K > 0 && p.Bgt > 0 && !cache->payload) return SSD_ERR_INVALID_ARG;
-    p.ckeys = cache->keys;
-    p.cpay = cache->payload;
-    p.chit = cache->out_hit;
-    p.cslot = cache->out_slot;
-    p.ctok = cache->out_tokens;
-    p.lookup = 1;
+  const ssd_verify_args a{target_logits, draft_logits, dt, B, K, V, ld, temperature, F, C, seed, draft_tokens,
+                          draft_q, draft_stats, draft_topf_idx, ld_topf, out_accept_len, out_bonus, out_p,
+                          out_target_stats, cache, workspace, ws_bytes};
+  Plan q;
+  const ssd_status s = plan_verify(a, q);
+  if (s != SSD_OK) return s;
+  (void)hipGetLastError();
+  return hip_status(launch_verify(q, (hipStream_t)stream));
+}
+
+ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream) {
+  if (!v && !s) return SSD_ERR_INVALID_ARG;
+  Plan qv, qs;
+  if (v) {
+    const ssd_status e = plan_verify(*v, qv);
+    if (e != SSD_OK) return e;
   }
-  Layout L;
-  if (!layout(SSD_OP_VERIFY, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
-  if (!ws_ok(workspace, ws_bytes, L)) return SSD_ERR_WORKSPACE;
-  const int64_t rows = (int64_t)B * (K + 1);
-  const int64_t NB = nblocks(V), nch = cdiv(NB, CH), nchr = cdiv(NB, CH_R);
-  if (rows * nch > kMaxGrid || (int64_t)B * nchr > kMaxGrid) return SSD_ERR_UNSUPPORTED;
-  p.x = (const unsigned char*)target_logits;
-  p.xd = (const unsigned char*)draft_logits;
-  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
-  p.K = K; p.B = B;
-  p.temp = temperature;
-  p.F = F; p.C = C; p.seed = seed;
-  char* ws = (char*)workspace;
-  p.part = (float4*)(ws + L.part);
-  p.state = (SeqState*)(ws + L.state);
-  p.rpart = (float2*)(ws + L.rpart);
-  p.stats = out_target_stats;
-  p.dtok = draft_tokens;
-  p.dq = draft_q;
-  p.zcap = (float*)(ws + L.zcap);
-  p.dstats = draft_stats;
-  p.dtopf = F > 0 ? draft_topf_idx : nullptr;
-  p.ld_dtopf = ld_topf;
-  p.acc_len = out_accept_len;
-  p.bonus = out_bonus;
-  p.p_out = out_p;
-  const bool al = aligned16(target_logits, ld, V, dt) && aligned16(draft_logits, ld, V, dt);
+  if (s) {
+    const ssd_status e = plan_sample(*s, qs);
+    if (e != SSD_OK) return e;
+  }
+  if (v && s && (v->workspace == s->workspace)) return SSD_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
+  if (!v) return hip_status(launch_sample(qs, st));
+  if (!s) return hip_status(launch_verify(qv, st));
+  if (qv.dt != qs.dt || qv.al != qs.al) {
+    // kernels of different element types cannot share a launch: in turn
+    hipError_t e = launch_verify(qv, st);
+    if (e == hipSuccess) e = launch_sample(qs, st);
+    return hip_status(e);
+  }
+  // verification's streaming pass; then its acceptance and residual pass
+  // beside sampling's streaming pass; then its bonus (and lookup) beside
+  // sampling's epilogue
+  Params pv = qv.p;
   hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
-    return dispatch<LVerify>(dt, al, rows * nch, p, st, e0, e1);
+    return dispatch<LVerify>(qv.dt, qv.al, qv.g_stream, pv, st, e0, e1);
   });
-  p.nchunk = (int)nchr;
-  if (e == hipSuccess) e = dispatch<LAccept>(dt, al, (int64_t)B * nchr, p, st);
-  if (e == hipSuccess) e = dispatch<LResidualEpi>(dt, al, B, p, st);
+  // fewer, longer residual workgroups: they share the GPU with the
+  // streaming pass, whose progress sets the launch's duration
+  pv.racc = CH_R * RACC_ROUND;
+  pv.nchunk = (int)cdiv(pv.NB, pv.racc);
+  const int64_t g_acc = (int64_t)pv.B * pv.nchunk;
+  if (e == hipSuccess) e = dispatch<LRoundMid>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st);
+  if (e == hipSuccess) e = dispatch<LRoundTail>(qv.dt, qv.al, qv.g_tail + qs.g_tail, pv, qs.p, (int)qv.g_tail, st);
   return hip_status(e);
 }
 

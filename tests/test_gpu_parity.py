@@ -251,3 +251,55 @@ def test_cache_keys_from_sampling_and_lookup_in_verify():
         assert np.array_equal(cache.slot.cpu().numpy(), os_)
         assert np.array_equal(cache.tokens.cpu().numpy(), ot)
         _say(f"  hits {int(oh.sum())} of {B}")
+
+
+ROUND_CASES = [
+    # B, K, V, dtype of verification, dtype of sampling, kind
+    (16, 7, 151936, BF16, BF16, "zipf"),     # merged launches
+    (5, 3, 20000, F16, F16, "peaks"),        # merged, fp16
+    (3, 2, 5001, F32, F32, "normal"),        # merged, unaligned rows
+    (4, 4, 40000, BF16, F32, "normal"),      # element types differ: one call after the other
+]
+
+
+@pytest.mark.parametrize("case", ROUND_CASES, ids=lambda c: f"B{c[0]}K{c[1]}V{c[2]}{DTNAME[c[3]]}{DTNAME[c[4]]}")
+def test_round_step_matches_separate_calls(case):
+    """ssd_round (verification of round i beside sampling of round i+1):
+    every output, cache keys and lookup included, identical to ssd_verify
+    followed by ssd_saguaro_sample."""
+    import lossless_verify_sample_amd as ssd
+    B, K, V, dtv, dts, kind = case
+    cv = W.custom(B, K, V, dtv, T=0.9, F=4, C=0.5, kind=kind, draft_sd=0.8, F_out=4)
+    cs = W.custom(B, K, V, dts, T=0.9, F=4, C=0.5, kind=kind, draft_sd=0.8, F_out=4)
+    T = torch.full((B,), 0.9, device=DEV)
+    T[0] = 0.0  # one greedy sequence
+    Fk = ssd.fanout(32, K, 0.6, V)
+    t, d = W.logits(cv, 0, DEV)
+    _, d1 = W.logits(cs, 1, DEV)
+    pay = W.payload(cv, 32, 0, DEV)
+    c0 = ssd.Cache(Fk, B, K, DEV, payload=pay, miss_fill=True)
+    s0 = ssd.saguaro_sample(d, T, 4, 0.5, 11, F_out=4, cache=c0)
+
+    def run(use_round):
+        c1 = ssd.Cache(Fk, B, K, DEV, payload=pay)
+        va = dict(target=t, draft=d, temperature=T, F=4, C=0.5, seed=11, tokens=s0["tokens"], draft_q=s0["q"],
+                  draft_stats=s0["stats"], draft_topf_idx=s0["topf_idx"], want_stats=True, cache=c0)
+        sa = dict(draft=d1, temperature=T, F=4, C=0.5, seed=12, F_out=4, cache=c1)
+        if use_round:
+            v, s = ssd.round_step(va, sa)
+        else:
+            v = ssd.verify(**va)
+            s = ssd.saguaro_sample(**sa)
+        torch.cuda.synchronize()
+        return ({k: x.clone() for k, x in v.items()}, {k: x.clone() for k, x in s.items()},
+                [c0.hit.clone(), c0.slot.clone(), c0.tokens.clone(), c1.keys.clone()])
+
+    v_ref, s_ref, c_ref = run(False)
+    v_got, s_got, c_got = run(True)
+    for k in v_ref:
+        assert torch.equal(v_got[k], v_ref[k]), k
+    for k in s_ref:
+        assert torch.equal(s_got[k], s_ref[k]), k
+    for a, b in zip(c_got, c_ref):
+        assert torch.equal(a, b)
+    _say(f"round {case[:3]}: accepted {v_ref['accept_len'].tolist()} hits {c_ref[0].tolist()}")

@@ -180,3 +180,48 @@ def test_backoff_rejects_bad_arguments(L):
                   ([0.5], {"t_slow": -1.0}), ([0.5], {"e_acc": 0.0}), ([0.5], {"e_fast": float("inf")})):
         with pytest.raises(ssd.SSDError):
             ssd.backoff(p, **dict(ok, **kw))
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of ssd_cache, ssd_sample_args, ssd_verify_args and
+    ssd_backoff_cost have the C sizes and field offsets (compiled with gcc)."""
+    import shutil
+    import subprocess
+    import lossless_verify_sample_amd as ssd
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    mirrors = {"ssd_cache": ssd._CacheStruct, "ssd_sample_args": ssd._SampleArgs,
+               "ssd_verify_args": ssd._VerifyArgs, "ssd_backoff_cost": ssd._BackoffCost}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssd.h"', "int main(void) {"]
+    for cname, py in mirrors.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        name, field, val = line.split()
+        got[(name, field)] = int(val)
+    for cname, py in mirrors.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_round_rejects_bad_arguments(L):
+    import lossless_verify_sample_amd as ssd
+    P = ctypes.c_void_p(1 << 20)
+    r = L.ssd_round
+    r.argtypes = [ctypes.c_void_p] * 3
+    assert r(None, None, None) == 1  # neither call
+    ws = ctypes.c_void_p(1 << 24)
+    v = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, None, None, ws, 1 << 24)
+    s = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 0.5, 2, 0, P, P, P, P, P, None, ws, 1 << 24)
+    assert r(ctypes.byref(v), ctypes.byref(s), None) == 3  # one workspace for both
+    bad = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 1.5, 2, 0, P, P, P, P, P, None, ws, 1 << 24)
+    assert r(None, ctypes.byref(bad), None) == 1  # C > 1
