@@ -180,6 +180,21 @@ __device__ __forceinline__ void load_raw(const unsigned char* row, int V, int be
   }
 }
 
+// Element k (static) of a packed block, decoded: the same value decode_raw
+// puts in v[k].
+template <int DT, bool AL>
+__device__ __forceinline__ float raw_elem(const RawBlock<DT, AL>& r, int k) {
+  if constexpr (DT == SSD_F32) return __uint_as_float(r.w[k]);
+  if constexpr (AL) {
+    const uint32_t w = r.w[k >> 1];
+    if constexpr (DT == SSD_BF16) return (k & 1) ? bf16hi(w) : bf16lo(w);
+    else return (k & 1) ? f16hi(w) : f16lo(w);
+  } else {
+    if constexpr (DT == SSD_BF16) return __uint_as_float(r.w[k] << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)r.w[k]);
+  }
+}
+
 template <int DT, bool AL>
 __device__ __forceinline__ void decode_raw(const RawBlock<DT, AL>& r, float (&v)[32]) {
   if constexpr (AL) {

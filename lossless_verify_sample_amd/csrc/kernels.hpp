@@ -763,7 +763,7 @@ __device__ __forceinline__ void epi_keys_p(const Params& p, int item, ESm& sm) {
 // max(0, p - sigma) over target row k* and draft row k*, in the target's
 // units scaled by exp(L_t) 2^(eps_t) (a constant per sequence), with the
 // target block maxima.
-template <int DT, bool AL, int PLN>
+template <int DT, bool AL, int PLN, int BPW>
 __device__ __forceinline__ void accept_residual(const Params& p, int b, int chunk, ESm& sm) {
   const int K = p.K, K1 = K + 1, NB = p.NB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -936,21 +936,16 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
   const unsigned char* rd = p.xd + row * rs;
   const float ot = ss.o_t, od = ss.o_d, nk = -ss.kf;
   const int64_t rrow = row * p.ld_dtopf;
-  auto residual = [&](const RawBlock<DT, AL>& ut, const RawBlock<DT, AL>& ud, int be) {
-    float vt[32], vd[32];
-    decode_raw<DT, AL>(ut, vt);
-    decode_raw<DT, AL>(ud, vd);
-    float g[32 / Dt<DT>::VW];
-#pragma unroll
-    for (int i = 0; i < 32 / Dt<DT>::VW; ++i) g[i] = group_max<Dt<DT>::VW>(&vt[i * Dt<DT>::VW]);
-    const float Mt = wave_max3(lane_max<32 / Dt<DT>::VW>(g));
+  // the target block maxima of row k* come from its streaming partials
+  const float4* tpart = p.part + (r0 + ks) * NB;
+  auto residual = [&](const RawBlock<DT, AL>& ut, const RawBlock<DT, AL>& ud, int be, float Mt) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 32; k += 2) {
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(vt[k], s, ot));
-      const float e2 = __builtin_amdgcn_exp2f(fmaf(vd[k], s, od));
-      const float f1 = __builtin_amdgcn_exp2f(fmaf(vt[k + 1], s, ot));
-      const float f2 = __builtin_amdgcn_exp2f(fmaf(vd[k + 1], s, od));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k), s, ot));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k), s, od));
+      const float f1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k + 1), s, ot));
+      const float f2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k + 1), s, od));
       a0 += fmaxf(fmaf(nk, e2, e1), 0.f);
       a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
     }
@@ -962,11 +957,11 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
       if (x >= 0 && x < V && x / BLK == be) {
         constexpr int VW = Dt<DT>::VW;
         const int off = x - be * BLK, gi = off / VW, kk = (gi >> 6) * VW + off % VW;
-        float zt = vt[0], zd = vd[0];
+        float zt = raw_elem<DT, AL>(ut, 0), zd = raw_elem<DT, AL>(ud, 0);
 #pragma unroll
         for (int k = 1; k < 32; ++k) {
-          zt = k == kk ? vt[k] : zt;
-          zd = k == kk ? vd[k] : zd;
+          zt = k == kk ? raw_elem<DT, AL>(ut, k) : zt;
+          zd = k == kk ? raw_elem<DT, AL>(ud, k) : zd;
         }
         zt = rl_f(zt, gi & 63);
         zd = rl_f(zd, gi & 63);
@@ -978,6 +973,21 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     if (lane == 0) p.rpart[(int64_t)b * NB + be] = make_float2(fmaxf(R, 0.f), Mt);
   };
   const int end = min(NB, (chunk + 1) * p.racc);
+  if constexpr (BPW == 1) {
+    // one block per wave at a time (fewer registers)
+    for (int be0 = chunk * p.racc + wave; be0 < end; be0 += ENW) {
+      RawBlock<DT, AL> ut0, ud0;
+      if ((be0 + 1) * BLK <= V) {
+        load_raw<DT, AL, true>(rt, V, be0, lane, ut0);
+        load_raw<DT, AL, true>(rd, V, be0, lane, ud0);
+      } else {
+        load_raw<DT, AL, false>(rt, V, be0, lane, ut0);
+        load_raw<DT, AL, false>(rd, V, be0, lane, ud0);
+      }
+      residual(ut0, ud0, be0, tpart[be0].x);
+    }
+    return;
+  }
   for (int base = chunk * p.racc; base < end; base += CH_R) {
     const int be0 = base + wave, be1 = be0 + ENW;
     if (be0 >= end) break;
@@ -993,8 +1003,9 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
       load_raw<DT, AL, false>(rt, V, min(be1, NB - 1), lane, ut1);
       load_raw<DT, AL, false>(rd, V, min(be1, NB - 1), lane, ud1);
     }
-    residual(ut0, ud0, be0);
-    if (be1 < end) residual(ut1, ud1, be1);
+    const float Mt0 = tpart[be0].x, Mt1 = tpart[min(be1, NB - 1)].x;
+    residual(ut0, ud0, be0, Mt0);
+    if (be1 < end) residual(ut1, ud1, be1, Mt1);
   }
 }
 
@@ -1135,17 +1146,20 @@ __global__ __launch_bounds__(EWG) void k_epi(Params p) {
 }
 
 // Acceptance and residual pass (one workgroup per sequence and chunk).
-template <int DT, bool AL>
+// BPW: residual blocks per wave in flight at a time (2: all of a standalone
+// workgroup's loads at once; 1: fewer registers, for the launch shared with
+// a streaming pass)
+template <int DT, bool AL, int BPW>
 __device__ __forceinline__ void accept_item(const Params& p, int item, ESm& sm) {
   const int b = item / p.nchunk, chunk = item - b * p.nchunk;
-  if (p.NB <= 128) accept_residual<DT, AL, 2>(p, b, chunk, sm);
-  else accept_residual<DT, AL, NBL>(p, b, chunk, sm);
+  if (p.NB <= 128) accept_residual<DT, AL, 2, BPW>(p, b, chunk, sm);
+  else accept_residual<DT, AL, NBL, BPW>(p, b, chunk, sm);
 }
 
 template <int DT, bool AL>
 __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(Params p) {
   __shared__ ESm sm;
-  accept_item<DT, AL>(p, blockIdx.x, sm);
+  accept_item<DT, AL, 2>(p, blockIdx.x, sm);
 }
 
 // Wave 0's copy of sequence b's keys and payload, one slot per lane, when
@@ -1269,7 +1283,7 @@ __global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
 template <int DT, bool AL>
 __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_round_mid(Params pv, Params ps, int nv) {
   __shared__ ESm sm;
-  if ((int)blockIdx.x < nv) accept_item<DT, AL>(pv, blockIdx.x, sm);
+  if ((int)blockIdx.x < nv) accept_item<DT, AL, 1>(pv, blockIdx.x, sm);
   else stream_item<DT, AL, M_SAMPLE>(ps, (int)blockIdx.x - nv);
 }
 
