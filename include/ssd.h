@@ -321,6 +321,22 @@ ssd_status ssd_cache_keys(const int32_t* topf_idx, int32_t ld_topf, const int32_
  *   finite or <= 0, V < 1, Bgt > (K+1)*V. */
 ssd_status ssd_fanout(int32_t Bgt, int32_t K, double ratio, int64_t V, int32_t* out_F);
 
+/* Fan-out from measured statistics ([SSD-B] part 1: the budget goes where
+ * acceptance stops most often; the pages' truncated geometric is the shape
+ * this gives when the hit curves are the same power law at every depth).
+ * Pure host function.
+ *   a      host double [K+1]: measured P(k* = k), finite, >= 0
+ *   h      host double [K+1][Fmax+1] row-major: h[k][F] = measured chance
+ *          that the bonus after k acceptances is among the draft's top-F
+ *          tokens of row k (h[k][0] = 0, non-decreasing in F), finite
+ *   Fmax   1 .. SSD_MAX_F; Bgt <= (K+1) Fmax
+ * Output out_F host int32 [K+1], sum Bgt: each slot in turn goes to the depth
+ * with the largest a[k] (h[k][F_k+1] - h[k][F_k]) (ties to the smaller k;
+ * depths at Fmax excluded); optimal for sum_k a[k] h[k][F_k] when every h[k]
+ * is concave.  Errors: SSD_ERR_INVALID_ARG. */
+ssd_status ssd_fanout_greedy(const double* a, const double* h, int32_t K, int32_t Fmax, int32_t Bgt,
+                             int32_t* out_F);
+
 /* Back-off rule for cache misses ([SSD-B] part 3: as the batch grows, the
  * chance that some sequence misses grows and the whole batch waits for the
  * backup speculator; below a critical batch size, set by the hit rate and the

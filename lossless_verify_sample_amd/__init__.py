@@ -15,7 +15,7 @@ import torch  # provides the process's HIP runtime, which libssd then shares
 
 __all__ = [
     "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "round_step", "cache_keys", "cache_lookup",
-    "fanout", "backoff", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
+    "fanout", "fanout_greedy", "backoff", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
@@ -116,6 +116,7 @@ def _load():
         "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _u64, _vp],
         "ssd_backoff": [_vp, _i32, _vp, _vp, _vp],
         "ssd_round": [_vp, _vp, _vp],
+        "ssd_fanout_greedy": [_vp, _vp, _i32, _i32, _i32, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
     }
@@ -392,6 +393,20 @@ def cache_lookup(keys, depth_off, payload, accept_len, bonus, miss_fill=False, V
                                  _p(hit), _p(slot), _p(toks), 1 if miss_fill else 0, int(V),
                                  int(seed) & (2 ** 64 - 1), _stream(dev)), "ssd_cache_lookup")
     return hit, slot, toks
+
+
+def fanout_greedy(a, h, Bgt):
+    """Fan-out F_0..F_K from measured depth probabilities a [K+1] and hit
+    curves h [K+1][Fmax+1] (host computation in libssd)."""
+    K1 = len(a)
+    Fmax = len(h[0]) - 1
+    if any(len(row) != Fmax + 1 for row in h) or len(h) != K1:
+        raise SSDError("h must be [K+1][Fmax+1]")
+    av = (ctypes.c_double * K1)(*[float(x) for x in a])
+    hv = (ctypes.c_double * (K1 * (Fmax + 1)))(*[float(x) for row in h for x in row])
+    out = (ctypes.c_int32 * K1)()
+    _check(_lib.ssd_fanout_greedy(av, hv, K1 - 1, Fmax, int(Bgt), out), "ssd_fanout_greedy")
+    return list(out)
 
 
 def backoff(p_hit, t_round, t_slow, t_fast, e_acc, e_fast):

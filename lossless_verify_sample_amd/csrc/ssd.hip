@@ -554,6 +554,35 @@ ssd_status ssd_fanout(int32_t Bgt, int32_t K, double ratio, int64_t V, int32_t* 
   return SSD_OK;
 }
 
+ssd_status ssd_fanout_greedy(const double* a, const double* h, int32_t K, int32_t Fmax, int32_t Bgt,
+                             int32_t* out_F) {
+  if (!a || !h || !out_F || K < 0 || K > SSD_MAX_K || Fmax < 1 || Fmax > SSD_MAX_F || Bgt < 0)
+    return SSD_ERR_INVALID_ARG;
+  if ((int64_t)Bgt > (int64_t)(K + 1) * Fmax) return SSD_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < (int64_t)(K + 1) * (Fmax + 1); ++i)
+    if (!std::isfinite(h[i])) return SSD_ERR_INVALID_ARG;
+  for (int k = 0; k <= K; ++k)
+    if (!std::isfinite(a[k]) || a[k] < 0.0) return SSD_ERR_INVALID_ARG;
+  std::vector<int32_t> F(K + 1, 0);
+  for (int32_t n = 0; n < Bgt; ++n) {
+    // the slot goes to the largest marginal gain; ties to the smaller depth
+    double best = -INFINITY;
+    int bk = -1;
+    for (int k = 0; k <= K; ++k) {
+      if (F[k] >= Fmax) continue;
+      const double* hk = h + (int64_t)k * (Fmax + 1);
+      const double g = a[k] * (hk[F[k] + 1] - hk[F[k]]);
+      if (g > best) {
+        best = g;
+        bk = k;
+      }
+    }
+    ++F[bk];
+  }
+  for (int k = 0; k <= K; ++k) out_F[k] = F[k];
+  return SSD_OK;
+}
+
 ssd_status ssd_backoff(const double* p_hit, int32_t B, const ssd_backoff_cost* c, int32_t* out_use_fast,
                        double* out_gain) {
   if (!p_hit || !c || !out_use_fast || B < 1) return SSD_ERR_INVALID_ARG;

@@ -377,6 +377,34 @@ def fanout_objective(a, r, F):
     return sum(a[k] * (1 - (1 + F[k]) ** -r) for k in range(len(a)))
 
 
+def fanout_from_stats(a, h, Bgt):
+    """Budget allocation from measured statistics ([SSD-B] part 1: spend the
+    cache budget where acceptance stops most often).  a[k]: measured
+    P(k* = k); h[k][F]: measured chance that the bonus at depth k is among
+    the draft's top-F tokens (F = 0 .. Fmax, h[k][0] = 0).  Each of the Bgt
+    slots goes to the depth with the largest gain a[k] (h[k][F_k + 1] -
+    h[k][F_k]), ties to the smaller k, depths already at Fmax excluded.
+    Maximises sum_k a[k] h[k][F_k] when every h[k] is concave."""
+    K1 = len(a)
+    Fmax = len(h[0]) - 1
+    if Bgt > K1 * Fmax:
+        raise ValueError("budget larger than (K+1) Fmax")
+    F = [0] * K1
+    for _ in range(Bgt):
+        best, bk = -math.inf, -1
+        for k in range(K1):
+            if F[k] < Fmax:
+                g = a[k] * (h[k][F[k] + 1] - h[k][F[k]])
+                if g > best:
+                    best, bk = g, k
+        F[bk] += 1
+    return F
+
+
+def fanout_stats_objective(a, h, F):
+    return sum(a[k] * h[k][F[k]] for k in range(len(a)))
+
+
 # --------------------------------------------------------------------------
 # speculation cache ([SSD-B] core-mechanism section: the draft fills a
 # speculation cache while verification runs, and one lookup follows when the

@@ -225,3 +225,24 @@ def test_round_rejects_bad_arguments(L):
     assert r(ctypes.byref(v), ctypes.byref(s), None) == 3  # one workspace for both
     bad = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 1.5, 2, 0, P, P, P, P, P, None, ws, 1 << 24)
     assert r(None, ctypes.byref(bad), None) == 1  # C > 1
+
+
+def test_fanout_greedy_matches_oracle(L):
+    """The host allocation from measured statistics against the oracle's on
+    random (also non-concave) curves: identical vectors."""
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        K1, Fmax = int(rng.integers(1, 9)), int(rng.integers(1, 40))
+        a = rng.dirichlet(np.ones(K1))
+        inc = rng.uniform(0, 1, (K1, Fmax))
+        if rng.random() < 0.5:
+            inc = np.sort(inc, axis=1)[:, ::-1]
+        h = np.concatenate([np.zeros((K1, 1)), np.cumsum(inc, axis=1)], axis=1) / Fmax
+        Bgt = int(rng.integers(0, K1 * Fmax + 1))
+        assert ssd.fanout_greedy(a, h.tolist(), Bgt) == O.fanout_from_stats(a, h.tolist(), Bgt)
+    with pytest.raises(ssd.SSDError):
+        ssd.fanout_greedy([0.5, 0.5], [[0, 1], [0, 1]], 3)   # budget above (K+1) Fmax
+    with pytest.raises(ssd.SSDError):
+        ssd.fanout_greedy([0.5, -0.1], [[0, 1], [0, 1]], 1)  # negative probability

@@ -107,3 +107,41 @@ def test_cache_lookup_brute_force():
         else:
             assert np.all(toks[b] == -1)
     assert hit.sum() > 5
+
+
+def _concave_curves(rng, K1, Fmax):
+    inc = np.sort(rng.uniform(0.0, 1.0, (K1, Fmax)), axis=1)[:, ::-1]
+    h = np.concatenate([np.zeros((K1, 1)), np.cumsum(inc, axis=1)], axis=1)
+    return h / h[:, -1:] * rng.uniform(0.3, 1.0, (K1, 1))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fanout_from_stats_is_optimal_on_concave_curves(seed):
+    # brute force over every allocation of the budget
+    rng = np.random.default_rng(seed)
+    K1, Fmax = int(rng.integers(2, 4)), 6
+    a = rng.dirichlet(np.ones(K1))
+    h = _concave_curves(rng, K1, Fmax)
+    for Bgt in range(0, K1 * Fmax + 1, 2):
+        F = O.fanout_from_stats(a, h, Bgt)
+        assert sum(F) == Bgt and max(F) <= Fmax
+        best = max(O.fanout_stats_objective(a, h, c)
+                   for c in itertools.product(range(Fmax + 1), repeat=K1) if sum(c) == Bgt)
+        assert O.fanout_stats_objective(a, h, F) >= best - 1e-12
+
+
+def test_fanout_from_stats_matches_the_parametric_model():
+    # measured curves equal to the model h(F) = 1 - (1+F)^-r give the model's allocation
+    r, Fmax = 0.7, 64
+    for alpha, K, Bgt in ((0.6, 5, 64), (0.8, 7, 100), (0.4, 3, 20)):
+        a = O.depth_probs(alpha, K)
+        h = [[1 - (1 + F) ** -r for F in range(Fmax + 1)] for _ in range(K + 1)]
+        assert O.fanout_from_stats(a, h, Bgt) == O.optimal_fanout(a, r, Bgt)
+
+
+def test_fanout_from_stats_ties_and_caps():
+    h = [[0.0, 0.5, 0.75], [0.0, 0.5, 0.75]]
+    assert O.fanout_from_stats([0.5, 0.5], h, 1) == [1, 0]   # tie: smaller depth
+    assert O.fanout_from_stats([0.9, 0.1], h, 3) == [2, 1]   # depth 0 capped at Fmax
+    with pytest.raises(ValueError):
+        O.fanout_from_stats([0.5, 0.5], h, 5)
