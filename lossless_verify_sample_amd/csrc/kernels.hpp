@@ -763,7 +763,7 @@ __device__ __forceinline__ void epi_keys_p(const Params& p, int item, ESm& sm) {
 // max(0, p - sigma) over target row k* and draft row k*, in the target's
 // units scaled by exp(L_t) 2^(eps_t) (a constant per sequence), with the
 // target block maxima.
-template <int DT, bool AL, int PLN, int BPW>
+template <int DT, bool AL, int PLN>
 __device__ __forceinline__ void accept_residual(const Params& p, int b, int chunk, ESm& sm) {
   const int K = p.K, K1 = K + 1, NB = p.NB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -973,21 +973,6 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     if (lane == 0) p.rpart[(int64_t)b * NB + be] = make_float2(fmaxf(R, 0.f), Mt);
   };
   const int end = min(NB, (chunk + 1) * p.racc);
-  if constexpr (BPW == 1) {
-    // one block per wave at a time (fewer registers)
-    for (int be0 = chunk * p.racc + wave; be0 < end; be0 += ENW) {
-      RawBlock<DT, AL> ut0, ud0;
-      if ((be0 + 1) * BLK <= V) {
-        load_raw<DT, AL, true>(rt, V, be0, lane, ut0);
-        load_raw<DT, AL, true>(rd, V, be0, lane, ud0);
-      } else {
-        load_raw<DT, AL, false>(rt, V, be0, lane, ut0);
-        load_raw<DT, AL, false>(rd, V, be0, lane, ud0);
-      }
-      residual(ut0, ud0, be0, tpart[be0].x);
-    }
-    return;
-  }
   for (int base = chunk * p.racc; base < end; base += CH_R) {
     const int be0 = base + wave, be1 = be0 + ENW;
     if (be0 >= end) break;
@@ -1146,20 +1131,17 @@ __global__ __launch_bounds__(EWG) void k_epi(Params p) {
 }
 
 // Acceptance and residual pass (one workgroup per sequence and chunk).
-// BPW: residual blocks per wave in flight at a time (2: all of a standalone
-// workgroup's loads at once; 1: fewer registers, for the launch shared with
-// a streaming pass)
-template <int DT, bool AL, int BPW>
+template <int DT, bool AL>
 __device__ __forceinline__ void accept_item(const Params& p, int item, ESm& sm) {
   const int b = item / p.nchunk, chunk = item - b * p.nchunk;
-  if (p.NB <= 128) accept_residual<DT, AL, 2, BPW>(p, b, chunk, sm);
-  else accept_residual<DT, AL, NBL, BPW>(p, b, chunk, sm);
+  if (p.NB <= 128) accept_residual<DT, AL, 2>(p, b, chunk, sm);
+  else accept_residual<DT, AL, NBL>(p, b, chunk, sm);
 }
 
 template <int DT, bool AL>
 __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(Params p) {
   __shared__ ESm sm;
-  accept_item<DT, AL, 2>(p, blockIdx.x, sm);
+  accept_item<DT, AL>(p, blockIdx.x, sm);
 }
 
 // Wave 0's copy of sequence b's keys and payload, one slot per lane, when
@@ -1283,7 +1265,7 @@ __global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
 template <int DT, bool AL>
 __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_round_mid(Params pv, Params ps, int nv) {
   __shared__ ESm sm;
-  if ((int)blockIdx.x < nv) accept_item<DT, AL, 1>(pv, blockIdx.x, sm);
+  if ((int)blockIdx.x < nv) accept_item<DT, AL>(pv, blockIdx.x, sm);
   else stream_item<DT, AL, M_SAMPLE>(ps, (int)blockIdx.x - nv);
 }
 

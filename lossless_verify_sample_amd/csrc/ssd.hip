@@ -109,7 +109,7 @@ bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
 }
 
 const int64_t kMaxGrid = 0x7fffffff;
-constexpr int RACC_ROUND = 5;  // residual blocks per workgroup in ssd_round, in units of CH_R
+constexpr int RACC_ROUND = 4;  // residual blocks per workgroup in ssd_round, in units of CH_R
 
 // Depth offsets of a cache descriptor into p (false for a bad fan-out).
 bool cache_layout(const ssd_cache* c, int K, int64_t V, Params& p) {
