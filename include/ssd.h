@@ -274,7 +274,9 @@ typedef struct {
  * cache keys must not be the verification's inputs or outputs (round i+1's
  * buffers are not round i's).  When the element types or the 16-byte
  * alignment of the two differ, the calls run one after the other.
- * Errors: as the two calls. */
+ * Errors: as the two calls; also SSD_ERR_INVALID_ARG when a sampling output
+ * (tokens, q, stats, top-F indices) is the verification's input of the same
+ * kind or both use the same cache keys (other aliasing is not detected). */
 ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream);
 
 /* Speculation-cache lookup keyed by (accepted length, bonus token) ([SSD-B]

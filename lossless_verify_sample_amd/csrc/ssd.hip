@@ -418,6 +418,15 @@ ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* s
     if (e != SSD_OK) return e;
   }
   if (v && s && (v->workspace == s->workspace)) return SSD_ERR_WORKSPACE;
+  if (v && s) {
+    // round i+1's sampling must not write what round i's verification reads
+    const void* w[] = {s->out_tokens, s->out_q, s->out_stats, s->out_topf_idx};
+    const void* r[] = {v->draft_tokens, v->draft_q, v->draft_stats, v->draft_topf_idx};
+    for (const void* a : w)
+      for (const void* b : r)
+        if (a && a == b) return SSD_ERR_INVALID_ARG;
+    if (v->cache && s->cache && v->cache->keys && v->cache->keys == s->cache->keys) return SSD_ERR_INVALID_ARG;
+  }
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   if (!v) return hip_status(launch_sample(qs, st));

@@ -225,6 +225,11 @@ def test_round_rejects_bad_arguments(L):
     assert r(ctypes.byref(v), ctypes.byref(s), None) == 3  # one workspace for both
     bad = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 1.5, 2, 0, P, P, P, P, P, None, ws, 1 << 24)
     assert r(None, ctypes.byref(bad), None) == 1  # C > 1
+    ws2 = ctypes.c_void_p(1 << 25)
+    Q = ctypes.c_void_p(1 << 26)
+    s2 = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 0.5, 2, 0, Q, Q, Q, Q, Q, None, ws2, 1 << 24)
+    v2 = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, Q, P, P, P, 2, P, P, P, None, None, ws, 1 << 24)
+    assert r(ctypes.byref(v2), ctypes.byref(s2), None) == 1  # sampling writes the tokens being verified
 
 
 def test_fanout_greedy_matches_oracle(L):
