@@ -259,6 +259,8 @@ ROUND_CASES = [
     (5, 3, 20000, F16, F16, "peaks"),        # merged, fp16
     (3, 2, 5001, F32, F32, "normal"),        # merged, unaligned rows
     (4, 4, 40000, BF16, F32, "normal"),      # element types differ: one call after the other
+    (256, 5, 128256, BF16, BF16, "peaks"),   # cache-scale batch
+    (512, 4, 151936, F16, F16, "zipf"),      # large batch, fp16
 ]
 
 
@@ -272,7 +274,7 @@ def test_round_step_matches_separate_calls(case):
     cv = W.custom(B, K, V, dtv, T=0.9, F=4, C=0.5, kind=kind, draft_sd=0.8, F_out=4)
     cs = W.custom(B, K, V, dts, T=0.9, F=4, C=0.5, kind=kind, draft_sd=0.8, F_out=4)
     T = torch.full((B,), 0.9, device=DEV)
-    T[0] = 0.0  # one greedy sequence
+    T[: max(1, B // 8)] = 0.0  # greedy sequences
     Fk = ssd.fanout(32, K, 0.6, V)
     t, d = W.logits(cv, 0, DEV)
     _, d1 = W.logits(cs, 1, DEV)
