@@ -2,26 +2,34 @@
 """Benchmark of the batched lossless verify-and-resample step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic logits:
-draft sampling with Saguaro sigma_{F,C} (ssd_saguaro_sample, which also
-writes the speculation-cache keys: each draft row's top-F_k list under the
-truncated-geometric fan-out), verification (ssd_verify: acceptance, accepted
-prefix, bonus, and the cache lookup of (k*, bonus)).  Default workload: B=64, K=7,
-V=151936 (Qwen-3 vocabulary), bf16 logits, T=1, F=4, C=0.5; cache budget 64
-with fan-out ratio 0.6.  Inputs rotate over > 1 GiB of distinct sets so the
-256 MB Infinity Cache cannot serve them.  Prints one JSON line.
+draft sampling with Saguaro sigma_{F,C} (which also writes the speculation-
+cache keys: each draft row's top-F_k list under the truncated-geometric
+fan-out) and verification (acceptance, accepted prefix, bonus, the cache
+lookup of (k*, bonus), misses filled with random tokens).  The headline runs
+the steps as SSD does, through ssd_round: step i's verification shares its
+launches with step i+1's sampling (every step still samples and verifies its
+own batch in full; results are checked equal to the separate calls, which
+are timed as well).  Default workload: B=64, K=7, V=151936 (Qwen-3
+vocabulary), bf16 logits, T=1, F=4, C=0.5; cache budget 64 with fan-out
+ratio 0.6.  Inputs rotate over > 1 GiB of distinct sets so the 256 MB
+Infinity Cache cannot serve them.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config N] [--no-cache] [--no-cpu-baseline]
   python bench.py --copy-gib G   (plain device copy of G GiB, for counter calibration)
 
-Roofline: the dominant kernel is the streaming pass (one read of every logit
-row) of sampling or verification, whichever takes longer.  After the timed
-steps the same steps run once more with the library's kernel timer on, which
-stamps each streaming launch with HIP events recorded by the launch itself on
-the call's stream (a separate pass because the event work slows the step).  Algorithmic bytes per launch = B (K+1) V element
-bytes read + one 16-byte partial per 2048-token block written (+ the drafted
-tokens and captured target logits for verification).  `traffic` comes from the
-rocprofv3 FETCH_SIZE / WRITE_SIZE summary committed under profiles/ for that
-kernel, and is null when the kernel sources changed since it was taken.
+Roofline: the dominant kernel of the headline schedule, the longer of its two
+HBM-bound launches: the shared launch k_round_mid (sampling's streaming pass
+beside the verification's residual pass) or the verification's streaming
+pass.  After the timed steps the same steps run again with the library's
+kernel timer on, which stamps those launches with HIP events recorded by the
+launch itself on the call's stream (separate passes, because the event work
+slows the step).  Algorithmic bytes: B (K+1) V element bytes read + one
+16-byte partial per 2048-token block written, + for the shared launch the
+draft row k* of every sequence with a residual and the residual block sums
+(+ for the verification stream the drafted tokens and captured logits).
+`traffic` comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary committed
+under profiles/ for that kernel, and is null when the kernel sources changed
+since it was taken.
 """
 import argparse
 import hashlib
@@ -218,6 +226,12 @@ def main():
         step(i, instrument=True)
     torch.cuda.synchronize()
     k_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
+    # and the headline schedule once more with the timer: there the sampling
+    # op is the shared launch (sampling stream + residual pass)
+    ssd.timer_enable(a.steps + 1)
+    run_rounds(a.warmup, total)
+    torch.cuda.synchronize()
+    r_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
     ssd.timer_enable(0)
     ms = start.elapsed_time(stop) / a.steps
     ms_sep = s0.elapsed_time(s1) / a.steps
@@ -234,15 +248,26 @@ def main():
     rows_per_s = cfg.rows / (ms * 1e-3)
     gbs_sample = b_sample / (t_s * 1e-3) / 1e9
     gbs_verify = b_verify / (t_v * 1e-3) / 1e9
-    # the dominant kernel: the longer of the two streaming passes
+    # per-launch times: streaming passes of the separate calls, and in the
+    # headline schedule the shared launch and the verification's stream
     k_ms = {op: (t / n if n else float("nan")) for op, (n, t) in k_launch.items()}
+    r_ms = {op: (t / n if n else float("nan")) for op, (n, t) in r_launch.items()}
     NB = -(-V // 2048)
-    k_bytes = {ssd.OP_SAMPLE: cfg.rows * row_bytes + cfg.rows * NB * 16,
-               ssd.OP_VERIFY: cfg.rows * row_bytes + cfg.rows * NB * 16 + 2 * B * K * 4 + B * K * 4}
-    dom = ssd.OP_SAMPLE if k_ms[ssd.OP_SAMPLE] >= k_ms[ssd.OP_VERIFY] else ssd.OP_VERIFY
+    s_bytes = cfg.rows * row_bytes + cfg.rows * NB * 16
+    v_bytes = cfg.rows * row_bytes + cfg.rows * NB * 16 + 2 * B * K * 4 + B * K * 4
+    # shared launch: sampling's stream + the draft row k* of every sequence
+    # with a residual (its target row k* is a re-read, not counted) + the
+    # residual block sums written
+    m_bytes = s_bytes + rej * row_bytes + B * NB * 8
     dtn = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[cfg.dtype]
-    kname = f"k_stream<{dtn},aligned,{'sample' if dom == ssd.OP_SAMPLE else 'verify'}>"
-    achieved = k_bytes[dom] / (k_ms[dom] * 1e-3) / 1e9
+    al = "aligned" if (V * esz) % 16 == 0 else "unaligned"
+    # the dominant kernel of the headline schedule: the longer of its two
+    # HBM-bound launches
+    if r_ms[ssd.OP_SAMPLE] >= r_ms[ssd.OP_VERIFY]:
+        kname, k_alg, k_t, k_n = f"k_round_mid<{dtn},{al}>", m_bytes, r_ms[ssd.OP_SAMPLE], r_launch[ssd.OP_SAMPLE][0]
+    else:
+        kname, k_alg, k_t, k_n = f"k_stream<{dtn},{al},verify>", v_bytes, r_ms[ssd.OP_VERIFY], r_launch[ssd.OP_VERIFY][0]
+    achieved = k_alg / (k_t * 1e-3) / 1e9
     traffic = recorded_traffic(kname)
     backoff = None
     if use_cache:
@@ -298,13 +323,17 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": k_bytes[dom],
-            "launches": k_launch[dom][0],
-            "ms_per_launch": round(k_ms[dom], 5),
+            "algorithmic_bytes": int(k_alg),
+            "launches": k_n,
+            "ms_per_launch": round(k_t, 5),
             "source": source_hash(),
         },
+        "ms_round_mid": round(r_ms[ssd.OP_SAMPLE], 5),
+        "ms_round_verify_stream": round(r_ms[ssd.OP_VERIFY], 5),
+        "residual_rows_per_step": round(rej, 2),
         "ms_stream_sample": round(k_ms[ssd.OP_SAMPLE], 5),
         "ms_stream_verify": round(k_ms[ssd.OP_VERIFY], 5),
+        "gbs_stream_sample": round(s_bytes / (k_ms[ssd.OP_SAMPLE] * 1e-3) / 1e9, 1),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, sets, T, Fo)

@@ -380,7 +380,9 @@ const char* ssd_status_string(ssd_status s);
  * once from HBM, in ssd_softmax_t, ssd_topf, ssd_saguaro_sample and
  * ssd_verify -- is timed by a pair of HIP events that the launch itself
  * records on the call's stream (hipExtLaunchKernelGGL), up to max_launches
- * launches per op.
+ * launches per op.  In ssd_round the launch that carries the sampling's
+ * streaming pass (beside the verification's residual pass) counts as
+ * SSD_OP_SAMPLE and the verification's streaming pass as SSD_OP_VERIFY.
  *   ssd_timer_enable(n): n > 0 (re)creates the events and clears the counts;
  *     n = 0 destroys them.  Host-side state of the library, not thread-safe:
  *     enable, read and disable from one thread while no call is in flight.

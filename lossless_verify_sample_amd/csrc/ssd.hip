@@ -100,6 +100,15 @@ SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
     }                                                                                     \
   };
 SSD_LAUNCHER2(LRoundMid, (k_round_mid<DT, AL>))
+// The same with the timer's events recorded by the launch.
+template <int DT, bool AL>
+struct LRoundMidT {
+  static hipError_t go(int64_t grid, const Params& pv, const Params& ps, int nv, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1) {
+    hipExtLaunchKernelGGL((k_round_mid<DT, AL>), dim3((unsigned)grid), dim3(EWG), 0, st, e0, e1, 0, pv, ps, nv);
+    return hipGetLastError();
+  }
+};
 SSD_LAUNCHER2(LRoundTail, (k_round_tail<DT, AL>))
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
@@ -449,7 +458,12 @@ ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* s
   pv.racc = CH_R * RACC_ROUND;
   pv.nchunk = (int)cdiv(pv.NB, pv.racc);
   const int64_t g_acc = (int64_t)pv.B * pv.nchunk;
-  if (e == hipSuccess) e = dispatch<LRoundMid>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st);
+  if (e == hipSuccess) {
+    e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
+      return e0 ? dispatch<LRoundMidT>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st, e0, e1)
+                : dispatch<LRoundMid>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st);
+    });
+  }
   if (e == hipSuccess) e = dispatch<LRoundTail>(qv.dt, qv.al, qv.g_tail + qs.g_tail, pv, qs.p, (int)qv.g_tail, st);
   return hip_status(e);
 }
