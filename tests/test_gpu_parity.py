@@ -259,6 +259,8 @@ ROUND_CASES = [
     (5, 3, 20000, F16, F16, "peaks"),        # merged, fp16
     (3, 2, 5001, F32, F32, "normal"),        # merged, unaligned rows
     (4, 4, 40000, BF16, F32, "normal"),      # element types differ: one call after the other
+    (3, 0, 3000, BF16, BF16, "normal"),      # K = 0: bonus only
+    (6, 3, 40000, F32, F32, "peaks"),        # aligned fp32
     (256, 5, 128256, BF16, BF16, "peaks"),   # cache-scale batch
     (512, 4, 151936, F16, F16, "zipf"),      # large batch, fp16
 ]
