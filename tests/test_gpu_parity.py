@@ -33,6 +33,8 @@ SMALL = [
     (2, 7, 40000, BF16, 1.0, 4, 0.5, 64, "normal", False),  # F_out = 64 > NB
     (4, 3, 16392, F32, 0.5, 4, 1.0, 4, "normal", False),    # C = 1, 8-element tail
     (3, 2, 70001, BF16, 2.0, 0, 0.5, 0, "normal", False),   # F = 0, odd V
+    (2, 2, 300000, BF16, 1.0, 4, 0.5, 27, "zipf", False),   # NB = 147 > 128: rows of 8 partials per lane
+    (2, 1, 1 << 20, F16, 0.8, 4, 0.5, 8, "normal", True),   # the largest vocabulary (NB = 512)
 ]
 
 
@@ -261,6 +263,7 @@ ROUND_CASES = [
     (4, 4, 40000, BF16, F32, "normal"),      # element types differ: one call after the other
     (3, 0, 3000, BF16, BF16, "normal"),      # K = 0: bonus only
     (6, 3, 40000, F32, F32, "peaks"),        # aligned fp32
+    (2, 3, 300000, BF16, BF16, "zipf"),      # NB > 128
     (256, 5, 128256, BF16, BF16, "peaks"),   # cache-scale batch
     (512, 4, 151936, F16, F16, "zipf"),      # large batch, fp16
 ]
