@@ -244,14 +244,18 @@ struct WRow {
 template <int PLN>
 __device__ __forceinline__ void load_wrow(const float4* pr, int NB, WRow<PLN>& r) {
   const int lane = threadIdx.x & 63;
+  // unconditional loads from clamped addresses, so that every slot's load is
+  // in flight at once (a load under a branch gets a wait of its own)
+  float4 v[PLN];
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) v[i] = pr[min(lane + 64 * i, NB - 1)];
 #pragma unroll
   for (int i = 0; i < PLN; ++i) {
-    const int be = lane + 64 * i;
-    const float4 v = be < NB ? pr[be] : make_float4(-INFINITY, 0.f, __int_as_float(-1), -INFINITY);
-    r.M[i] = v.x;
-    r.S[i] = v.y;
-    r.I[i] = __float_as_int(v.z);
-    r.M2[i] = v.w;
+    const bool in = lane + 64 * i < NB;
+    r.M[i] = in ? v[i].x : -INFINITY;
+    r.S[i] = in ? v[i].y : 0.f;
+    r.I[i] = in ? __float_as_int(v[i].z) : -1;
+    r.M2[i] = in ? v[i].w : -INFINITY;
   }
 }
 
@@ -400,10 +404,29 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
     for (int c0 = tid; c0 < BLK / VW; c0 += EWG) {  // chunk c0 of every re-read block
       for (int k0 = 0; k0 < nrb; k0 += RB) {
         float v[RB][VW];
+        if constexpr (AL) {
+          // all RB loads are issued before any is decoded (left to itself the
+          // scheduler interleaves them with the decoding, two loads in flight)
+          uint4 w[RB];
 #pragma unroll
-        for (int u = 0; u < RB; ++u) {
-          const int e0 = sm.rblk[min(k0 + u, nrb - 1)] * BLK + c0 * VW;
-          load_chunk<DT, AL>(rp, V, e0, v[u]);
+          for (int u = 0; u < RB; ++u) {
+            const int e0 = sm.rblk[min(k0 + u, nrb - 1)] * BLK + c0 * VW;
+            w[u] = *reinterpret_cast<const uint4*>(rp + (size_t)(e0 < V ? e0 : 0) * Dt<DT>::SZ);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            const int e0 = sm.rblk[min(k0 + u, nrb - 1)] * BLK + c0 * VW;
+            decode16<DT>(w[u], v[u]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) v[u][e] = e0 < V ? v[u][e] : -INFINITY;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            const int e0 = sm.rblk[min(k0 + u, nrb - 1)] * BLK + c0 * VW;
+            load_chunk<DT, AL>(rp, V, e0, v[u]);
+          }
         }
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
@@ -1011,12 +1034,14 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
   const int any = __syncthreads_or(R[0] > 0.f || R[1] > 0.f);
   float M[NBT], S[NBT];
   if (!any) {  // no residual mass: p_k* from the target row's partials
+    float4 v[NBT];
+#pragma unroll
+    for (int k = 0; k < NBT; ++k) v[k] = p.part[row * NB + min(tid + k * EWG, NB - 1)];
 #pragma unroll
     for (int k = 0; k < NBT; ++k) {
-      const int be = tid + k * EWG;
-      const float4 v = be < NB ? p.part[row * NB + be] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
-      M[k] = v.x;
-      S[k] = v.y;
+      const bool in = tid + k * EWG < NB;
+      M[k] = in ? v[k].x : -INFINITY;
+      S[k] = in ? v[k].y : 0.f;
     }
   }
   int beta = block_stage(NB, p.seed, b, ks, ST_BONUS_BLOCK, sm.ru[0], [&](int, int k) -> float {
@@ -1224,13 +1249,16 @@ __device__ __forceinline__ void residual_item(const Params& p, int b, ESm& sm) {
   const int NB = p.NB;
   // the residual sums (used only when the state asks for them), the state,
   // and the outcome of sequences decided earlier are loaded together
+  // (unconditional loads from clamped addresses: all in flight at once)
   float R[NBT], Mt[NBT];
+  float2 rv[NBT];
+#pragma unroll
+  for (int k = 0; k < NBT; ++k) rv[k] = p.rpart[(int64_t)b * NB + min((int)threadIdx.x + k * EWG, NB - 1)];
 #pragma unroll
   for (int k = 0; k < NBT; ++k) {
-    const int be = threadIdx.x + k * EWG;
-    const float2 v = be < NB ? p.rpart[(int64_t)b * NB + be] : make_float2(0.f, -INFINITY);
-    R[k] = v.x;
-    Mt[k] = v.y;
+    const bool in = (int)threadIdx.x + k * EWG < NB;
+    R[k] = in ? rv[k].x : 0.f;
+    Mt[k] = in ? rv[k].y : -INFINITY;
   }
   const SeqState ss = p.state[b];
   const int ks0 = p.lookup ? p.acc_len[b] : 0, y0 = p.lookup ? p.bonus[b] : 0;
