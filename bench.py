@@ -69,10 +69,11 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel):
-    """HBM bytes per launch of `kernel` from its committed counter summary
-    (profiles/*.md line 'traffic: kernel=... source=... fetch_bytes=...
-    write_bytes=...'), if it was taken on the current sources."""
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from its committed
+    counter summary (profiles/*.md line 'traffic: kernel=... workload=...
+    source=... fetch_bytes=... write_bytes=...'), if it was taken on the
+    current sources."""
     pdir = os.path.join(ROOT, "profiles")
     if not os.path.isdir(pdir):
         return None
@@ -83,7 +84,7 @@ def recorded_traffic(kernel):
             if not line.startswith("traffic:"):
                 continue
             kv = dict(x.split("=", 1) for x in line.split()[1:])
-            if kv.get("kernel") == kernel and kv.get("source") == source_hash():
+            if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("source") == source_hash():
                 return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
     return None
 
@@ -268,7 +269,7 @@ def main():
     else:
         kname, k_alg, k_t, k_n = f"k_stream<{dtn},{al},verify>", v_bytes, r_ms[ssd.OP_VERIFY], r_launch[ssd.OP_VERIFY][0]
     achieved = k_alg / (k_t * 1e-3) / 1e9
-    traffic = recorded_traffic(kname)
+    traffic = recorded_traffic(kname, cfg.name)
     backoff = None
     if use_cache:
         # back-off rule on the measured per-sequence hit rates: a round costs
