@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from lossless_verify_sample_amd import workloads as W
+from oracle import ssd as O
 from parity import DTNAME, Report, check_round, raw_host, stats_np
 
 pytestmark = pytest.mark.gpu
@@ -137,19 +138,45 @@ def test_repeat_calls_are_bit_identical():
         assert np.array_equal(a[1][k], b[1][k]), k
 
 
+def _accept_law(zt, zd, T, F, C):
+    """Exact law of k* for fixed logits: acceptance at position j, once
+    reached, has probability alpha_j = sum_x min(p_j(x), sigma_j(x)) and the
+    positions are independent.  Returns (E[k*], Var[k*])."""
+    K = zd.shape[0] - 1
+    alpha = [O.acceptance_rate(O.softmax_t(zt[j], T)["p"], O.sigma(zd[j], T, F, C)["sigma"]) for j in range(K)]
+    pk, reach = [], 1.0
+    for j in range(K):
+        pk.append(reach * (1.0 - alpha[j]))
+        reach *= alpha[j]
+    pk.append(reach)
+    k = np.arange(K + 1)
+    mean = float(np.dot(pk, k))
+    return mean, float(np.dot(pk, (k - mean) ** 2))
+
+
 def test_tiny_verify_workload():
-    """B=1, K=4, V=1000 fp32, T=1, F=2, C=0.5: 250 independent steps."""
+    """B=1, K=4, V=1000 fp32, T=1, F=2, C=0.5: 1000 independent steps.
+    Every unit bit-exact against the oracle outside near ties, near ties
+    under 1e-4 of the units, and the accepted lengths consistent with their
+    exact law (sum of k* - E[k*] within 5 standard deviations)."""
     cfg = W.CONFIGS[1]
     rep = Report()
-    acc = []
-    for step in range(250):
+    dev_sum, var_sum, acc = 0.0, 0.0, []
+    T = W.temperatures(cfg, DEV)
+    for step in range(1000):
         t, d = W.logits(cfg, step, DEV)
-        r, g_s, g_v, *_ = check_round(t, d, W.temperatures(cfg, DEV), cfg.F, cfg.C, W.seed(cfg, step),
-                                      workers=1)
+        r, g_s, g_v, *_ = check_round(t, d, T, cfg.F, cfg.C, W.seed(cfg, step), workers=1)
         rep.add(r)
-        acc.append(int(g_v["accept_len"][0]))
-    _say(f"tiny: units {rep.units} near {rep.near} mean accepted {np.mean(acc):.3f}")
+        k = int(g_v["accept_len"][0])
+        acc.append(k)
+        m, v = _accept_law(O.decode(raw_host(t[0]), "f32"), O.decode(raw_host(d[0]), "f32"), cfg.T, cfg.F, cfg.C)
+        dev_sum += k - m
+        var_sum += v
+    z = dev_sum / math.sqrt(var_sum)
+    _say(f"tiny: units {rep.units} near {rep.near} mean accepted {np.mean(acc):.3f} z {z:.2f}")
     assert rep.ok(), rep.fails
+    assert rep.near < 1e-4 * rep.units, (rep.near, rep.units)
+    assert abs(z) < 5.0, z
 
 
 @pytest.mark.parametrize("c", [2, 3, 4, 5])
