@@ -327,6 +327,15 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   const uint32_t c = __builtin_amdgcn_readlane((int)x, 32), d = __builtin_amdgcn_readlane((int)x, 48);
   return min(min(a, b), min(c, d));
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<DPP_XOR1>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_XOR2>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_HMIR>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_MIR>((int)x));
+  const uint32_t a = __builtin_amdgcn_readlane((int)x, 0), b = __builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane((int)x, 32), d = __builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
+}
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
   x = umin64(x, dpp_u64<DPP_XOR1>(x));
   x = umin64(x, dpp_u64<DPP_XOR2>(x));

@@ -31,6 +31,7 @@ constexpr int TPT = BLK / EWG;    // tokens per epilogue thread in a token stage
 constexpr int NBT = MAX_NB / EWG; // blocks per epilogue thread
 constexpr int NBL = MAX_NB / 64;  // blocks per lane when a wave holds a whole row
 static_assert(TPT == 8 && NBT == 2, "epilogue layout assumes 256 threads over 2048-token blocks");
+constexpr int KTH_ROUNDS = 8;     // top-F threshold by maximum rounds up to this F, by radix search above
 constexpr int TF_CAP = EWG;       // (K+1)*F draft top-F entries prefetched into LDS when they fit
 
 // What verification hands to the residual pass for one sequence.
@@ -311,6 +312,31 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&key)[PLN], int Fs, 
   return tk;
 }
 
+// The same for small Fs: rounds of a wave maximum, each removing every copy
+// of the largest remaining key and counting them, until Fs keys are counted
+// (at most Fs rounds, each a short DPP reduction instead of a chain of
+// ballot counts per bit pair).
+template <int PLN>
+__device__ __forceinline__ uint32_t kth_key_rounds(const uint32_t (&key)[PLN], int Fs) {
+  uint32_t k[PLN];
+#pragma unroll
+  for (int i = 0; i < PLN; ++i) k[i] = key[i];
+  uint32_t mx = 0;
+  int cum = 0;
+  for (int r = 0; r < Fs; ++r) {
+    uint32_t lm = k[0];
+#pragma unroll
+    for (int i = 1; i < PLN; ++i) lm = max(lm, k[i]);
+    mx = wave_max_u32(lm);
+#pragma unroll
+    for (int i = 0; i < PLN; ++i) cum += __popcll(__ballot(k[i] == mx));
+    if (cum >= Fs || mx == 0u) break;
+#pragma unroll
+    for (int i = 0; i < PLN; ++i) k[i] = k[i] == mx ? 0u : k[i];
+  }
+  return mx;
+}
+
 // Exact top-Fs of a row (value desc, index asc) from a wave's copy of its
 // partials.  The block maxima and second values are values of 2 NB distinct
 // elements, so tau, the Fs-th largest of them, bounds the Fs-th largest
@@ -339,7 +365,9 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
     kmin = in ? min(kmin, key[PLN + i]) : kmin;
   }
   const bool sel = 2 * NB > Fs;
-  const uint32_t tk = sel ? kth_key<2 * PLN>(key, Fs, ord_key(m), wave_min_u32(kmin), LowBit<DT>::B) : 0u;
+  const uint32_t tk = !sel ? 0u
+                    : Fs <= KTH_ROUNDS ? kth_key_rounds<2 * PLN>(key, Fs)
+                                       : kth_key<2 * PLN>(key, Fs, ord_key(m), wave_min_u32(kmin), LowBit<DT>::B);
   const float tau = sel ? ord_val(tk) : -INFINITY;
   bool cand[PLN], one[PLN];
   uint64_t more = 0;
