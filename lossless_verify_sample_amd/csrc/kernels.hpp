@@ -553,38 +553,70 @@ __device__ __forceinline__ int block_stage(int NB, uint64_t seed, int b, int j, 
 }
 
 // TPT consecutive elements x0.. of a row; past V reads as -inf.
+// The TPT tokens x0 .. x0 + TPT - 1 of a token stage (past V: -inf), in two
+// steps so that independent work can be placed while the loads are in
+// flight: run_issue starts the loads, run_finish decodes.  On the aligned
+// path the row holds 16-byte chunks (V and x0 are multiples of the chunk,
+// so a chunk lies wholly inside the row or wholly past it), loaded
+// unconditionally from clamped addresses (a load under a branch gets a wait
+// of its own).
 template <int DT, bool AL>
-__device__ __forceinline__ void load_run(const unsigned char* rp, int V, int x0, float (&z)[TPT]) {
+struct Run {
+  static constexpr int VW = Dt<DT>::VW, NC = TPT / VW;
+  uint4 w[AL ? NC : 1];
+  float z[AL ? 1 : TPT];
+};
+template <int DT, bool AL>
+__device__ __forceinline__ void run_issue(const unsigned char* rp, int V, int x0, Run<DT, AL>& r) {
   if constexpr (AL) {
-    if (x0 + TPT <= V) {
-      const uint4* a = reinterpret_cast<const uint4*>(rp + (size_t)x0 * Dt<DT>::SZ);
-      if constexpr (DT == SSD_F32) {
-        decode16<DT>(a[0], &z[0]);
-        decode16<DT>(a[1], &z[4]);
-      } else {
-        decode16<DT>(a[0], z);
-      }
-      return;
+#pragma unroll
+    for (int c = 0; c < Run<DT, AL>::NC; ++c) {
+      const int e0 = x0 + c * Run<DT, AL>::VW;
+      r.w[c] = *reinterpret_cast<const uint4*>(rp + (size_t)(e0 < V ? e0 : 0) * Dt<DT>::SZ);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < TPT; ++e) {
+      const bool in = x0 + e < V;
+      const float x = load_elem<DT>(rp, in ? x0 + e : 0);
+      r.z[e] = in ? x : -INFINITY;
     }
   }
+}
+template <int DT, bool AL>
+__device__ __forceinline__ void run_finish(int V, int x0, const Run<DT, AL>& r, float (&z)[TPT]) {
+  if constexpr (AL) {
+    constexpr int VW = Run<DT, AL>::VW;
 #pragma unroll
-  for (int e = 0; e < TPT; ++e) {
-    const bool in = x0 + e < V;
-    const float x = load_elem<DT>(rp, in ? x0 + e : 0);
-    z[e] = in ? x : -INFINITY;
+    for (int c = 0; c < Run<DT, AL>::NC; ++c) {
+      const int e0 = x0 + c * VW;
+      decode16<DT>(r.w[c], &z[c * VW]);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) z[c * VW + e] = e0 < V ? z[c * VW + e] : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < TPT; ++e) z[e] = r.z[e];
   }
 }
 
+// The Philox words of a token stage's TPT tokens (stream st at (b, j)).
+struct RaceWords {
+  uint32_t w[TPT];
+};
+__device__ __forceinline__ RaceWords race_words(int x0, uint64_t seed, int b, int j, uint32_t st) {
+  const uint4 wa = draws4(seed, (uint32_t)(x0 >> 2), (uint32_t)b, (uint32_t)j, st);
+  const uint4 wb = draws4(seed, (uint32_t)(x0 >> 2) + 1u, (uint32_t)b, (uint32_t)j, st);
+  return RaceWords{{wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w}};
+}
+
 // Token stage of the two-level draw over a block: thread t holds tokens
-// x0 .. x0 + TPT - 1 (x0 = beta*BLK + TPT*t) with their Philox words; tfn(e)
+// x0 .. x0 + TPT - 1 (x0 = beta*BLK + TPT*t) with their Philox words rw; tfn(e)
 // gives the log2 of the inverse weight of token x0 + e up to a constant
 // common to the block (+inf excludes it).  Returns the winner (-1 if none).
 template <class TF>
-__device__ __forceinline__ int token_race(int x0, int V, uint64_t seed, int b, int j, uint32_t st, uint64_t* slot,
-                                          TF tfn) {
-  const uint4 wa = draws4(seed, (uint32_t)(x0 >> 2), (uint32_t)b, (uint32_t)j, st);
-  const uint4 wb = draws4(seed, (uint32_t)(x0 >> 2) + 1u, (uint32_t)b, (uint32_t)j, st);
-  const uint32_t w[TPT] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+__device__ __forceinline__ int token_race(int x0, int V, const RaceWords& rw, uint64_t* slot, TF tfn) {
+  const uint32_t* w = rw.w;
   uint64_t best = NO_KEY;
 #pragma unroll
   for (int e = 0; e < TPT; ++e) {
@@ -757,12 +789,16 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   const int beta = bk == NO_KEY ? 0 : (int)(uint32_t)bk;  // no block of mass only for invalid rows
   // token stage over block beta
   const int x0 = beta * BLK + TPT * tid;
-  float z[TPT];
-  load_run<DT, AL>(rp, V, x0, z);
+  Run<DT, AL> run;
+  run_issue<DT, AL>(rp, V, x0, run);
+  const RaceWords rw = race_words(x0, p.seed, b, j, ST_DRAFT_TOKEN);  // while the block loads
   const uint32_t smask = set_mask_lanes(ti, F, x0);
+  __builtin_amdgcn_sched_barrier(0);
+  float z[TPT];
+  run_finish<DT, AL>(V, x0, run, z);
   const float nc2 = -__builtin_amdgcn_logf(C);  // -log2 C >= 0
   const float Mb = slot_at<PLN>(r.M, beta);
-  const int x = token_race(x0, V, p.seed, b, j, ST_DRAFT_TOKEN, sm.ru[1], [&](int e) -> float {
+  const int x = token_race(x0, V, rw, sm.ru[1], [&](int e) -> float {
     if (!(z[e] > -INFINITY)) return INFINITY;
     return (Mb - z[e]) * s + (((smask >> e) & 1u) ? nc2 : 0.f);
   });
@@ -970,10 +1006,14 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     if (beta < 0) beta = 0;
     const unsigned char* rp = p.x + (r0 + K) * rs;
     const int x0 = beta * BLK + TPT * tid;
+    Run<DT, AL> run;
+    run_issue<DT, AL>(rp, V, x0, run);
+    const RaceWords rw = race_words(x0, p.seed, b, K, ST_BONUS_TOKEN);  // while the block loads
+    __builtin_amdgcn_sched_barrier(0);
     float z[TPT];
-    load_run<DT, AL>(rp, V, x0, z);
+    run_finish<DT, AL>(V, x0, run, z);
     const float Mb = sm.M[beta];
-    const int x = token_race(x0, V, p.seed, b, K, ST_BONUS_TOKEN, sm.ru[1], [&](int e) -> float {
+    const int x = token_race(x0, V, rw, sm.ru[1], [&](int e) -> float {
       return z[e] > -INFINITY ? (Mb - z[e]) * s : INFINITY;
     });
     if (tid == 0) p.bonus[b] = x >= 0 ? x : 0;
@@ -1077,9 +1117,14 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
   });
   if (beta < 0) beta = 0;
   const int x0 = beta * BLK + TPT * tid;
+  Run<DT, AL> runt, rund;
+  run_issue<DT, AL>(rt, V, x0, runt);
+  run_issue<DT, AL>(rd, V, x0, rund);
+  const RaceWords rw = race_words(x0, p.seed, b, ks, ST_BONUS_TOKEN);  // while the blocks load
+  __builtin_amdgcn_sched_barrier(0);
   float zt[TPT], zd[TPT];
-  load_run<DT, AL>(rt, V, x0, zt);
-  load_run<DT, AL>(rd, V, x0, zd);
+  run_finish<DT, AL>(V, x0, runt, zt);
+  run_finish<DT, AL>(V, x0, rund, zd);
   const float Mb = sm.M[beta];
   int x = -1;
   if (any) {
@@ -1087,7 +1132,7 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
     const uint32_t smask = F <= 0 ? 0u : tf_lds ? set_mask(sm.tf + ks * F, F, x0)
                                                 : set_mask(p.dtopf + row * p.ld_dtopf, F, x0);
     const double invT = ss.invT, D0 = ss.D0, lnC = ss.lnC;
-    x = token_race(x0, V, p.seed, b, ks, ST_BONUS_TOKEN, sm.ru[1], [&](int e) -> float {
+    x = token_race(x0, V, rw, sm.ru[1], [&](int e) -> float {
       if (!(zt[e] > -INFINITY)) return INFINITY;
       const float tp = (Mb - zt[e]) * s;
       if (!(zd[e] > -INFINITY)) return tp;
@@ -1098,7 +1143,7 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
   }
   if (x < 0) {
     // no residual mass, or the chosen block had mass only through rounding: p there
-    x = token_race(x0, V, p.seed, b, ks, ST_BONUS_TOKEN, sm.ru[2], [&](int e) -> float {
+    x = token_race(x0, V, rw, sm.ru[2], [&](int e) -> float {
       return zt[e] > -INFINITY ? (Mb - zt[e]) * s : INFINITY;
     });
   }
