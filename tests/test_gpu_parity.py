@@ -193,6 +193,7 @@ def test_full_size_workload(c):
              f"mean k* {g_v['accept_len'].mean():.3f}")
         del t, d
     assert rep.ok(), rep.fails
+    assert rep.near < 1e-4 * rep.units, (rep.near, rep.units)
 
 
 def test_cache_lookup_against_oracle():
