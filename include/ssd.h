@@ -261,6 +261,22 @@ typedef struct {
   size_t ws_bytes;
 } ssd_verify_args;
 
+/* Verification with early exit ([SSD-A]: the target keeps the drafted tokens
+ * only up to the first rejection, so no target row past it influences the
+ * result): the same acceptance test, accepted length, bonus and cache lookup
+ * as ssd_verify on the same arguments (`a`, as in ssd_verify), reading fewer
+ * target rows.  Positions 0 .. J-1 are streamed for every sequence; positions
+ * J .. K only for the sequences with no clear rejection below J (a decision
+ * taken conservatively from the rows already read: u_j at least rho_j (1 +
+ * 1e-4), a greedy token that is not the argmax, or a token outside [0, V)),
+ * so a sequence whose acceptance test reaches row J always has its later
+ * rows read.  1 <= J <= K+1 (J = K+1 reads every row).
+ * Differences from ssd_verify: out_p[b, j] is p_j(x_j) for j <= k* and NaN
+ * past it; out_target_stats must be NULL.  Workspace as for ssd_verify.
+ * Errors: as ssd_verify; also SSD_ERR_INVALID_ARG for a NULL `a`, J outside
+ * [1, K+1] or out_target_stats not NULL. */
+ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream);
+
 /* One step of the SSD pipeline ([SSD-A] and [SSD-B] core mechanism: the draft
  * speculates the next round while the target verifies the current one):
  * verification of round i (`v`) and draft sampling of round i+1 (`s`), with

@@ -14,7 +14,7 @@ import os
 import torch  # provides the process's HIP runtime, which libssd then shares
 
 __all__ = [
-    "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "round_step", "cache_keys", "cache_lookup",
+    "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "verify_early", "round_step", "cache_keys", "cache_lookup",
     "fanout", "fanout_greedy", "backoff", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
 ]
 
@@ -116,6 +116,7 @@ def _load():
         "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _u64, _vp],
         "ssd_backoff": [_vp, _i32, _vp, _vp, _vp],
         "ssd_round": [_vp, _vp, _vp],
+        "ssd_verify_early": [_vp, _i32, _vp],
         "ssd_fanout_greedy": [_vp, _vp, _i32, _i32, _i32, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
@@ -337,6 +338,24 @@ def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats,
         return out, args
     _check(_lib.ssd_verify(*args, _stream(dev)), "ssd_verify")
     return out
+
+
+def verify_early(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats, draft_topf_idx, J=None,
+                 out=None, cache=None):
+    """Verification with early exit (ssd_verify_early): the results of
+    verify() on the same arguments, streaming target positions J .. K only
+    for sequences without a clear rejection below J (default J = min(3, K+1)).
+    out["p"][b, j] is NaN past the accepted length; no row statistics."""
+    B, K1, V = target.shape
+    J = min(3, K1) if J is None else int(J)
+    keep = []
+    if out is not None and out.get("stats") is not None:
+        raise SSDError("verify_early writes no row statistics")
+    o, a = verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats, draft_topf_idx,
+                  out=out, cache=cache, _defer=keep)
+    va = _VerifyArgs(*a)
+    _check(_lib.ssd_verify_early(ctypes.byref(va), J, _stream(target.device)), "ssd_verify_early")
+    return o
 
 
 def round_step(verify_args=None, sample_args=None):

@@ -56,6 +56,8 @@ struct Params {
   int64_t rows;             // rows streamed by the kernel
   int NB, nchunk;           // blocks per row, workgroups per row
   int racc;                 // verification: blocks per workgroup of the residual pass (a multiple of CH_R)
+  int jlo, jn;              // jn > 0: the streaming pass covers positions jlo .. jlo + jn - 1 of every sequence
+  int early;                // verification: rows past the first rejection may not have been streamed
   int K, B;
   const float* temp;
   int F, F_out, F_sel;
@@ -954,9 +956,10 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
         acc = (double)uacc < rho;
       }
     }
-    if (lead && lane < K) p.p_out[b * K + lane] = (float)pj;
     const uint64_t rej = __ballot(lane < K && !acc);
     const int ks = rej ? (int)__builtin_ctzll(rej) : K;
+    // (early exit: the rows past k* may not have been read)
+    if (lead && lane < K) p.p_out[b * K + lane] = (p.early && lane > ks) ? __builtin_nanf("") : (float)pj;
     SeqState ss{};
     if (!greedy && ks < K) {
       // hand-over to the residual pass (values of target and draft row k*)
@@ -1159,8 +1162,9 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
 // (f32 and unaligned rows need more registers per element: fewer waves)
 template <int DT, bool AL, int MODE>
 __device__ __forceinline__ void stream_item(const Params& p, int item) {
-  const int64_t row = item / p.nchunk;
-  const int chunk = item - (int)(row * p.nchunk);
+  const int64_t it = item / p.nchunk;
+  const int chunk = item - (int)(it * p.nchunk);
+  const int64_t row = p.jn > 0 ? (it / p.jn) * (p.K + 1) + p.jlo + (it % p.jn) : it;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K1 = p.K + 1;
   const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
@@ -1206,6 +1210,86 @@ __device__ __forceinline__ void stream_item(const Params& p, int item) {
 template <int DT, bool AL, int MODE>
 __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(Params p) {
   stream_item<DT, AL, MODE>(p, blockIdx.x);
+}
+
+// Early-exit verification.  A sequence's verification never reads target
+// rows past its first rejection, so once positions 0 .. J-1 have been
+// streamed, the rows from J on are needed only by sequences without a
+// rejection below J.  seq_alive judges that from the partials of rows < J
+// (written by the previous launch) conservatively: false only when some
+// position j < J is rejected with a clear margin (T > 0: u_j >= rho_j (1 +
+// 1e-4); greedy: x_j is not the row's argmax; or x_j outside [0, V)), so a
+// sequence that the acceptance pass may find unrejected below J is never
+// skipped.  Every thread calls; the result is uniform.
+struct GateSm {
+  float m[MAX_K1];
+  double L[MAX_K1];
+  int am[MAX_K1];
+  int alive;
+};
+template <int PLN>
+__device__ __forceinline__ bool seq_alive(const Params& p, int b, int J, GateSm& g) {
+  const int K = p.K, K1 = K + 1, NB = p.NB, V = (int)p.V;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float T = p.temp[b];
+  const bool greedy = !(T > 0.f);
+  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
+  const int Jd = min(J, K);  // positions with a decision
+  for (int j = wave; j < Jd; j += NWAVE) {
+    WRow<PLN> r;
+    load_wrow<PLN>(p.part + ((int64_t)b * K1 + j) * NB, NB, r);
+    float lm = r.M[0];
+#pragma unroll
+    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+    const float m = wave_max(lm);
+    double ws = 0.0;
+    int am = -1;
+#pragma unroll
+    for (int i = PLN - 1; i >= 0; --i) {
+      if (!greedy) ws += (double)block_w(r.M[i], r.S[i], m, s);
+      const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
+      if (mk) am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
+    }
+    ws = wave_sum_d(ws);
+    if (lane == 0) {
+      g.m[j] = m;
+      g.L[j] = greedy ? 0.0 : ln_fast(ws);
+      g.am[j] = am < 0 ? 0 : am;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    bool rej = false;
+    if (lane < Jd) {
+      const int xj = p.dtok[b * K + lane];
+      if (xj < 0 || xj >= V) {
+        rej = true;
+      } else if (greedy) {
+        rej = xj != g.am[lane];
+      } else {
+        const double pj = exp_fast(((double)p.zcap[b * K + lane] - (double)g.m[lane]) * (1.0 / (double)T) - g.L[lane]);
+        const double q = (double)p.dq[b * K + lane];
+        const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
+        const double u = (double)uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
+        rej = u >= rho * (1.0 + 1e-4) + 1e-30;
+      }
+    }
+    const uint64_t rm = __ballot(rej);
+    if (lane == 0) g.alive = rm == 0ull;
+  }
+  __syncthreads();
+  return g.alive != 0;
+}
+
+// Streaming pass of verification over positions jlo .. jlo + jn - 1, for the
+// sequences that seq_alive keeps (the others' workgroups return at once).
+template <int DT, bool AL>
+__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream_gated(Params p) {
+  __shared__ GateSm g;
+  const int b = (int)((blockIdx.x / p.nchunk) / p.jn);
+  const bool alive = p.NB <= 128 ? seq_alive<2>(p, b, p.jlo, g) : seq_alive<NBL>(p, b, p.jlo, g);
+  if (!alive) return;
+  stream_item<DT, AL, M_VERIFY>(p, blockIdx.x);
 }
 
 // Sampling epilogue item g: row g, or (g >= rows) a long cache-key list.

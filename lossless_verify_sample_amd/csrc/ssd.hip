@@ -83,6 +83,7 @@ SSD_LAUNCHER(LSoftmax, (k_stream<DT, AL, M_SOFTMAX>))
 SSD_LAUNCHER(LTopf, (k_stream<DT, AL, M_TOPF>))
 SSD_LAUNCHER(LSample, (k_stream<DT, AL, M_SAMPLE>))
 SSD_LAUNCHER(LVerify, (k_stream<DT, AL, M_VERIFY>))
+SSD_LAUNCHER(LVerifyGated, (k_stream_gated<DT, AL>))
 SSD_LAUNCHER_E(LSoftmaxEpi, (k_epi<DT, AL, M_SOFTMAX>))
 SSD_LAUNCHER_E(LTopfEpi, (k_epi<DT, AL, M_TOPF>))
 SSD_LAUNCHER_E(LSampleEpi, (k_epi<DT, AL, M_SAMPLE>))
@@ -413,6 +414,37 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   if (s != SSD_OK) return s;
   (void)hipGetLastError();
   return hip_status(launch_verify(q, (hipStream_t)stream));
+}
+
+ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
+  if (!a) return SSD_ERR_INVALID_ARG;
+  Plan q;
+  const ssd_status s = plan_verify(*a, q);
+  if (s != SSD_OK) return s;
+  const int K1 = q.p.K + 1;
+  if (J < 1 || J > K1 || a->out_target_stats) return SSD_ERR_INVALID_ARG;
+  const int64_t nch = q.p.nchunk;
+  if ((int64_t)q.p.B * K1 * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  // positions 0 .. J-1 of every sequence; then J .. K of the sequences that
+  // have no clear rejection below J; then acceptance, residual and bonus
+  Params p = q.p;
+  p.early = 1;
+  p.jlo = 0;
+  p.jn = J;
+  hipError_t e = dispatch<LVerify>(q.dt, q.al, (int64_t)p.B * J * nch, p, st);
+  if (e == hipSuccess && J < K1) {
+    Params pg = p;
+    pg.jlo = J;
+    pg.jn = K1 - J;
+    e = dispatch<LVerifyGated>(q.dt, q.al, (int64_t)p.B * (K1 - J) * nch, pg, st);
+  }
+  p.jn = 0;
+  p.nchunk = q.nch_accept;
+  if (e == hipSuccess) e = dispatch<LAccept>(q.dt, q.al, q.g_accept, p, st);
+  if (e == hipSuccess) e = dispatch<LResidualEpi>(q.dt, q.al, q.g_tail, p, st);
+  return hip_status(e);
 }
 
 ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream) {

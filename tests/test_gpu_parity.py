@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import lossless_verify_sample_amd as ssd
 from lossless_verify_sample_amd import workloads as W
 from oracle import ssd as O
 from parity import DTNAME, Report, check_round, raw_host, stats_np
@@ -177,6 +178,77 @@ def test_tiny_verify_workload():
     assert rep.ok(), rep.fails
     assert rep.near < 1e-4 * rep.units, (rep.near, rep.units)
     assert abs(z) < 5.0, z
+
+
+EARLY = [
+    # B, K, V, dtype, T, F, C, kind, greedy_half, J
+    (4, 3, 5000, BF16, 0.9, 4, 0.6, "peaks", False, 1),     # ragged bf16, only position 0 up front
+    (6, 5, 20000, F16, 1.3, 8, 0.3, "zipf", True, 2),       # greedy half
+    (3, 4, 5001, F32, 1.0, 2, 0.5, "normal", False, 3),     # unaligned fp32
+    (8, 7, 40000, BF16, 1.0, 4, 0.5, "zipf", False, 8),     # J = K + 1: every row up front
+    (5, 2, 300000, BF16, 1.0, 4, 0.5, "zipf", False, 2),    # NB > 128
+    (2, 0, 3000, BF16, 1.0, 2, 0.5, "normal", False, 1),    # K = 0
+]
+
+
+def _check_early(t, d, T, F, C, seed, J, F_out=None, workers=None, cache=None):
+    """verify_early against verify (bit for bit: k*, bonus, p up to k*, NaN
+    past it, cache outputs) and against the oracle (k*, bonus outside near
+    ties), on the same inputs and drafted tokens."""
+    r, g_s, g_v, smp, ver, o = check_round(t, d, T, F, C, seed, F_out=F_out, workers=workers)
+    assert r.ok(), r.fails
+    if cache is not None:
+        ssd.verify(t, d, T, F, C, seed, smp["tokens"], smp["q"], smp["stats"], smp["topf_idx"], cache=cache)
+        torch.cuda.synchronize()
+        ref_c = [x.clone() for x in (cache.hit, cache.slot, cache.tokens)]
+    e = ssd.verify_early(t, d, T, F, C, seed, smp["tokens"], smp["q"], smp["stats"], smp["topf_idx"], J=J,
+                         cache=cache)
+    torch.cuda.synchronize()
+    acc = e["accept_len"].cpu().numpy()
+    assert np.array_equal(acc, g_v["accept_len"])
+    assert np.array_equal(e["bonus"].cpu().numpy(), g_v["bonus"])
+    p = e["p"].cpu().numpy().astype(np.float64)
+    B, K = p.shape
+    for b in range(B):
+        assert np.array_equal(p[b, :acc[b] + 1], g_v["p"][b, :acc[b] + 1]), b
+        assert np.all(np.isnan(p[b, acc[b] + 1:])), b
+    ov = o["verify"]
+    for b in range(B):
+        if np.any(ov["acc_margin"][b] < 1e-5):
+            continue
+        assert acc[b] == ov["accept_len"][b], b
+        assert ov["bonus_margin"][b] < 1e-5 or e["bonus"][b].item() == ov["bonus"][b], b
+    if cache is not None:
+        for x, y in zip((cache.hit, cache.slot, cache.tokens), ref_c):
+            assert torch.equal(x, y)
+    return acc
+
+
+@pytest.mark.parametrize("case", EARLY, ids=lambda c: f"B{c[0]}K{c[1]}V{c[2]}{DTNAME[c[3]]}J{c[9]}")
+def test_verify_early(case):
+    B, K, V, dt, T, F, C, kind, gh, J = case
+    cfg = W.custom(B, K, V, dt, T=T, F=F, C=C, kind=kind, draft_sd=0.7, greedy_half=gh)
+    for step in range(4):
+        _say(f"verify_early {cfg.name} J={J} step {step}")
+        t, d = W.logits(cfg, step, DEV)
+        _check_early(t, d, W.temperatures(cfg, DEV), F, C, W.seed(cfg, step), J, workers=1)
+
+
+@pytest.mark.parametrize("c,J", [(3, 3), (5, 2)])
+def test_verify_early_full_size(c, J):
+    """Early exit on the Qwen-3-vocabulary (with the cache lookup) and the
+    large mixed greedy/sampled workload."""
+    cfg = W.CONFIGS[c]
+    t, d = W.logits(cfg, 0, DEV)
+    cache = None
+    if c == 3:
+        Fk = ssd.fanout(64, cfg.K, 0.6, cfg.V)
+        cache = ssd.Cache(Fk, cfg.B, cfg.K, DEV, payload=W.payload(cfg, 64, 0, DEV), miss_fill=True)
+        cache.keys.copy_(torch.randint(0, cfg.V, cache.keys.shape, device=DEV, dtype=torch.int32))
+    acc = _check_early(t, d, W.temperatures(cfg, DEV), cfg.F, cfg.C, W.seed(cfg, 0), J, F_out=cfg.fout,
+                       cache=cache)
+    _say(f"verify_early config {c}: sequences reading past position {J - 1}: "
+         f"{int((acc >= J).sum())} of {cfg.B} (at least)")
 
 
 @pytest.mark.parametrize("c", [2, 3, 4, 5])
