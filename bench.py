@@ -43,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD specification
+EARLY_J = 2            # positions streamed for every sequence by ssd_verify_early
 
 
 def parse():
@@ -154,7 +155,12 @@ def main():
     smp_out = smp_bufs[0]
     bonus = torch.empty(B, dtype=torch.int32, device=dev)
     pout = torch.empty((B, K), dtype=torch.float32, device=dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    early_out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+                     bonus=torch.empty(B, dtype=torch.int32, device=dev),
+                     p=torch.empty((B, K), dtype=torch.float32, device=dev), stats=None)
+
+    early_same = []
 
     def step(i, instrument=False):
         t, d = sets[i % nsets]
@@ -173,6 +179,12 @@ def main():
                    smp_out["topf_idx"], out=ver_out, cache=cache)
         if e:
             e[2].record()
+            # the same verification with early exit (timed only here; its
+            # accepted lengths must be the same)
+            ssd.verify_early(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["q"], smp_out["stats"],
+                             smp_out["topf_idx"], J=EARLY_J, out=early_out)
+            e[3].record()
+            early_same.append((early_out["accept_len"] == acc_buf[i]).all())  # checked after the pass
 
     # Headline schedule (ssd_round): step i's verification shares launches
     # with step i + 1's sampling, as the draft speculates the next round
@@ -239,6 +251,9 @@ def main():
     timed = range(a.warmup, total)
     t_s = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed) / a.steps
     t_v = sum(ev[i][1].elapsed_time(ev[i][2]) for i in timed) / a.steps
+    t_ve = sum(ev[i][2].elapsed_time(ev[i][3]) for i in timed) / a.steps
+    if not bool(torch.stack(early_same).all().item()):
+        raise SystemExit("ssd_verify_early gave other accepted lengths than ssd_verify")
     acc = acc_buf[a.warmup:].to(torch.int64)
     tokens = int((acc + 1).sum().item())
     # residual row pairs per step: T > 0 sequences with k* < K
@@ -312,6 +327,8 @@ def main():
         "mean_accepted": round(float(acc.float().mean().item()), 4),
         "ms_sample": round(t_s, 5),
         "ms_verify": round(t_v, 5),
+        "ms_verify_early": round(t_ve, 5),
+        "early_exit_J": EARLY_J,
         "gbs_sample": round(gbs_sample, 1),
         "gbs_verify": round(gbs_verify, 1),
         "cache_hit_rate": round(float(hit_buf[a.warmup:].sum().item()) / (a.steps * B), 4) if use_cache else None,

@@ -344,10 +344,10 @@ def verify_early(target, draft, temperature, F, C, seed, tokens, draft_q, draft_
                  out=None, cache=None):
     """Verification with early exit (ssd_verify_early): the results of
     verify() on the same arguments, streaming target positions J .. K only
-    for sequences without a clear rejection below J (default J = min(3, K+1)).
+    for sequences without a clear rejection below J (default J = min(2, K+1)).
     out["p"][b, j] is NaN past the accepted length; no row statistics."""
     B, K1, V = target.shape
-    J = min(3, K1) if J is None else int(J)
+    J = min(2, K1) if J is None else int(J)
     keep = []
     if out is not None and out.get("stats") is not None:
         raise SSDError("verify_early writes no row statistics")
