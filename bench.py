@@ -20,10 +20,13 @@ Infinity Cache cannot serve them.  Prints one JSON line.
 Roofline: the dominant kernel of the headline schedule, the longer of its two
 HBM-bound launches: the shared launch k_round_mid (sampling's streaming pass
 beside the verification's residual pass) or the verification's streaming
-pass.  After the timed steps the same steps run again with the library's
-kernel timer on, which stamps those launches with HIP events recorded by the
-launch itself on the call's stream (separate passes, because the event work
-slows the step).  Algorithmic bytes: B (K+1) V element bytes read + one
+pass.  After the timed steps each entry point runs again over the same
+steps back to back (sampling, verification, verification with early exit),
+timed with events around each loop (ms_sample, ms_verify, ms_verify_early)
+and with the library's kernel timer on, which stamps the streaming launches
+with HIP events recorded by the launch itself on the call's stream; the
+headline schedule runs once more with the timer for the shared launch
+(separate passes, because the event work slows the step).  Algorithmic bytes: B (K+1) V element bytes read + one
 16-byte partial per 2048-token block written, + for the shared launch the
 draft row k* of every sequence with a residual and the residual block sums
 (+ for the verification stream the drafted tokens and captured logits).
@@ -155,36 +158,16 @@ def main():
     smp_out = smp_bufs[0]
     bonus = torch.empty(B, dtype=torch.int32, device=dev)
     pout = torch.empty((B, K), dtype=torch.float32, device=dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
-    early_out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
-                     bonus=torch.empty(B, dtype=torch.int32, device=dev),
-                     p=torch.empty((B, K), dtype=torch.float32, device=dev), stats=None)
-
-    early_same = []
-
-    def step(i, instrument=False):
+    def step(i):
         t, d = sets[i % nsets]
         seed = W.seed(cfg, i)
-        e = ev[i] if instrument else None
-        if e:
-            e[0].record()
         cache = caches[i % nsets] if use_cache else None
         if cache is not None:
             cache.hit = hit_buf[i]
         ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=Fo, out=smp_out, cache=cache)
-        if e:
-            e[1].record()
         ver_out = dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None)
         ssd.verify(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["q"], smp_out["stats"],
                    smp_out["topf_idx"], out=ver_out, cache=cache)
-        if e:
-            e[2].record()
-            # the same verification with early exit (timed only here; its
-            # accepted lengths must be the same)
-            ssd.verify_early(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["q"], smp_out["stats"],
-                             smp_out["topf_idx"], J=EARLY_J, out=early_out)
-            e[3].record()
-            early_same.append((early_out["accept_len"] == acc_buf[i]).all())  # checked after the pass
 
     # Headline schedule (ssd_round): step i's verification shares launches
     # with step i + 1's sampling, as the draft speculates the next round
@@ -231,14 +214,45 @@ def main():
     same = bool(torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:]))
     if not same:
         raise SystemExit("ssd_round gave other accepted lengths or cache hits than the separate calls")
-    # instrumented pass: the same steps again with per-call events and the
-    # streaming launches stamped by their own events (kept out of the headline
-    # pass, whose step time the event work would inflate)
+    # per-call pass: each entry point over all the timed steps back to back
+    # (the host enqueues ahead, so the times are the GPU's), with per-step
+    # sampling outputs and cache keys, and the streaming launches stamped by
+    # the library's kernel timer (kept out of the headline pass, whose step
+    # time the event work would inflate); then the same verifications with
+    # early exit, whose accepted lengths must be the same
+    timed = range(a.warmup, total)
+    smp_all = [smp_buffers() for _ in timed]
+    caches_t = ([ssd.Cache(Fk, B, K, dev, payload=caches[i % nsets].payload, miss_fill=True) for i in timed]
+                if use_cache else [None] * a.steps)
+    acc_early = torch.zeros((a.steps, B), dtype=torch.int32, device=dev)
+    out_early = dict(bonus=torch.empty(B, dtype=torch.int32, device=dev),
+                     p=torch.empty((B, K), dtype=torch.float32, device=dev), stats=None)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     ssd.timer_enable(a.steps)
-    for i in range(a.warmup, total):
-        step(i, instrument=True)
+    ev[0].record()
+    for n, i in enumerate(timed):
+        ssd.saguaro_sample(sets[i % nsets][1], T, cfg.F, cfg.C, W.seed(cfg, i), F_out=Fo, out=smp_all[n],
+                           cache=caches_t[n])
+    ev[1].record()
+    for n, i in enumerate(timed):
+        t, d = sets[i % nsets]
+        sm = smp_all[n]
+        if caches_t[n] is not None:
+            caches_t[n].hit = hit_buf[i]
+        ssd.verify(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"], sm["topf_idx"],
+                   out=dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None), cache=caches_t[n])
+    ev[2].record()
+    for n, i in enumerate(timed):
+        t, d = sets[i % nsets]
+        sm = smp_all[n]
+        ssd.verify_early(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"], sm["topf_idx"],
+                         J=EARLY_J, out=dict(out_early, accept_len=acc_early[n]))
+    ev[3].record()
     torch.cuda.synchronize()
     k_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
+    if not (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:])
+            and torch.equal(acc_early, acc_buf[a.warmup:])):
+        raise SystemExit("the per-call pass or ssd_verify_early gave other accepted lengths or cache hits")
     # and the headline schedule once more with the timer: there the sampling
     # op is the shared launch (sampling stream + residual pass)
     ssd.timer_enable(a.steps + 1)
@@ -248,12 +262,9 @@ def main():
     ssd.timer_enable(0)
     ms = start.elapsed_time(stop) / a.steps
     ms_sep = s0.elapsed_time(s1) / a.steps
-    timed = range(a.warmup, total)
-    t_s = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed) / a.steps
-    t_v = sum(ev[i][1].elapsed_time(ev[i][2]) for i in timed) / a.steps
-    t_ve = sum(ev[i][2].elapsed_time(ev[i][3]) for i in timed) / a.steps
-    if not bool(torch.stack(early_same).all().item()):
-        raise SystemExit("ssd_verify_early gave other accepted lengths than ssd_verify")
+    t_s = ev[0].elapsed_time(ev[1]) / a.steps
+    t_v = ev[1].elapsed_time(ev[2]) / a.steps
+    t_ve = ev[2].elapsed_time(ev[3]) / a.steps
     acc = acc_buf[a.warmup:].to(torch.int64)
     tokens = int((acc + 1).sum().item())
     # residual row pairs per step: T > 0 sequences with k* < K
