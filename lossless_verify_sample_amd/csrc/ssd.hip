@@ -120,6 +120,7 @@ bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
 
 const int64_t kMaxGrid = 0x7fffffff;
 constexpr int RACC_ROUND = 4;  // residual blocks per workgroup in ssd_round, in units of CH_R
+constexpr int64_t kResidualWgs = 2048;  // fewest residual workgroups of a standalone verification
 
 // Depth offsets of a cache descriptor into p (false for a bad fan-out).
 bool cache_layout(const ssd_cache* c, int K, int64_t V, Params& p) {
@@ -263,7 +264,13 @@ ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
   if (!layout(SSD_OP_VERIFY, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
   if (!ws_ok(a.workspace, a.ws_bytes, L)) return SSD_ERR_WORKSPACE;
   const int64_t rows = (int64_t)B * (K + 1);
-  const int64_t NB = nblocks(V), nch = cdiv(NB, CH), nchr = cdiv(NB, CH_R);
+  // residual workgroups of CH_R blocks, or 2 or 4 times that while at least
+  // kResidualWgs of them remain (measured: longer ones merge the partials
+  // fewer times at large batches; shorter ones spread small batches wider)
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
+  int racc = CH_R;
+  while (racc < 4 * CH_R && (int64_t)B * cdiv(NB, 2 * racc) >= kResidualWgs) racc *= 2;
+  const int64_t nchr = cdiv(NB, racc);
   if (rows * nch > kMaxGrid || (int64_t)B * nchr > kMaxGrid) return SSD_ERR_UNSUPPORTED;
   p.x = (const unsigned char*)a.target_logits;
   p.xd = (const unsigned char*)a.draft_logits;
@@ -290,7 +297,7 @@ ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
   q.g_stream = rows * nch;
   q.g_accept = (int64_t)B * nchr;
   q.nch_accept = (int)nchr;
-  p.racc = CH_R;
+  p.racc = racc;
   q.g_tail = B;
   return SSD_OK;
 }
