@@ -251,3 +251,24 @@ def test_fanout_greedy_matches_oracle(L):
         ssd.fanout_greedy([0.5, 0.5], [[0, 1], [0, 1]], 3)   # budget above (K+1) Fmax
     with pytest.raises(ssd.SSDError):
         ssd.fanout_greedy([0.5, -0.1], [[0, 1], [0, 1]], 1)  # negative probability
+
+
+def test_verify_early_rejects_bad_arguments(L):
+    """ssd_verify_early checks everything ssd_verify checks, plus J in
+    [1, K+1] and no row statistics, before any launch."""
+    import lossless_verify_sample_amd as ssd
+    P = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 24)
+    f = L.ssd_verify_early
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, 1, None) == 1
+    # B = 2, K = 3, V = 100; out_target_stats NULL
+    v = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, None, None, ws, 1 << 24)
+    for J in (0, -1, 5):
+        assert f(ctypes.byref(v), J, None) == 1, J
+    with_stats = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, P, None, ws, 1 << 24)
+    assert f(ctypes.byref(with_stats), 2, None) == 1
+    small_ws = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, None, None, ws, 64)
+    assert f(ctypes.byref(small_ws), 2, None) == 3
+    bad_c = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 1.5, 0, P, P, P, P, 2, P, P, P, None, None, ws, 1 << 24)
+    assert f(ctypes.byref(bad_c), 2, None) == 1
