@@ -22,9 +22,11 @@ HBM-bound launches: the shared launch k_round_mid (sampling's streaming pass
 beside the verification's residual pass) or the verification's streaming
 pass.  After the timed steps each entry point runs again over the same
 steps back to back (sampling, verification, verification with early exit),
-timed with events around each loop (ms_sample, ms_verify, ms_verify_early)
-and with the library's kernel timer on, which stamps the streaming launches
-with HIP events recorded by the launch itself on the call's stream; the
+with the library's kernel timer on, which stamps the streaming launches
+with HIP events recorded by the launch itself on the call's stream; each of
+those loops is then captured in a HIP graph and replayed (every replay
+checked against the eager results) for the per-call times ms_sample,
+ms_verify and ms_verify_early, free of the Python binding's host path; the
 headline schedule runs once more with the timer for the shared launch
 (separate passes, because the event work slows the step).  Algorithmic bytes: B (K+1) V element bytes read + one
 16-byte partial per 2048-token block written, + for the shared launch the
@@ -227,32 +229,73 @@ def main():
     acc_early = torch.zeros((a.steps, B), dtype=torch.int32, device=dev)
     out_early = dict(bonus=torch.empty(B, dtype=torch.int32, device=dev),
                      p=torch.empty((B, K), dtype=torch.float32, device=dev), stats=None)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    def loop_sample():
+        for n, i in enumerate(timed):
+            ssd.saguaro_sample(sets[i % nsets][1], T, cfg.F, cfg.C, W.seed(cfg, i), F_out=Fo, out=smp_all[n],
+                               cache=caches_t[n])
+
+    def loop_verify():
+        for n, i in enumerate(timed):
+            t, d = sets[i % nsets]
+            sm = smp_all[n]
+            if caches_t[n] is not None:
+                caches_t[n].hit = hit_buf[i]
+            ssd.verify(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"], sm["topf_idx"],
+                       out=dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None), cache=caches_t[n])
+
+    def loop_early():
+        for n, i in enumerate(timed):
+            t, d = sets[i % nsets]
+            sm = smp_all[n]
+            ssd.verify_early(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"],
+                             sm["topf_idx"], J=EARLY_J, out=dict(out_early, accept_len=acc_early[n]))
+
+    def results_match():
+        return (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:])
+                and torch.equal(acc_early, acc_buf[a.warmup:]))
+
     ssd.timer_enable(a.steps)
-    ev[0].record()
-    for n, i in enumerate(timed):
-        ssd.saguaro_sample(sets[i % nsets][1], T, cfg.F, cfg.C, W.seed(cfg, i), F_out=Fo, out=smp_all[n],
-                           cache=caches_t[n])
-    ev[1].record()
-    for n, i in enumerate(timed):
-        t, d = sets[i % nsets]
-        sm = smp_all[n]
-        if caches_t[n] is not None:
-            caches_t[n].hit = hit_buf[i]
-        ssd.verify(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"], sm["topf_idx"],
-                   out=dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None), cache=caches_t[n])
-    ev[2].record()
-    for n, i in enumerate(timed):
-        t, d = sets[i % nsets]
-        sm = smp_all[n]
-        ssd.verify_early(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"], sm["topf_idx"],
-                         J=EARLY_J, out=dict(out_early, accept_len=acc_early[n]))
-    ev[3].record()
+    loop_sample()
+    loop_verify()
+    loop_early()
     torch.cuda.synchronize()
     k_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
-    if not (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:])
-            and torch.equal(acc_early, acc_buf[a.warmup:])):
+    ssd.timer_enable(0)
+    if not results_match():
         raise SystemExit("the per-call pass or ssd_verify_early gave other accepted lengths or cache hits")
+    # per-call times on the GPU: each loop captured once in a HIP graph (at
+    # small batches the binding's host path is slower than the GPU) and
+    # replayed several times, every replay checked against the eager results
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # the binding's workspaces for this stream, before capture
+        loop_sample()
+        loop_verify()
+        loop_early()
+    side.synchronize()
+    graphs = []
+    for fn in (loop_sample, loop_verify, loop_early):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fn()
+        graphs.append(g)
+    side.synchronize()
+    call_ms = [[], [], []]
+    for rep_ in range(3):
+        acc_buf[a.warmup:].fill_(-1)
+        acc_early.fill_(-1)
+        hit_buf[a.warmup:].fill_(-1)
+        torch.cuda.synchronize()
+        for k, g in enumerate(graphs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(side):
+                e0.record()
+                g.replay()
+                e1.record()
+            side.synchronize()
+            call_ms[k].append(e0.elapsed_time(e1) / a.steps)
+        if not results_match():
+            raise SystemExit(f"graph replay {rep_} gave other accepted lengths or cache hits")
     # and the headline schedule once more with the timer: there the sampling
     # op is the shared launch (sampling stream + residual pass)
     ssd.timer_enable(a.steps + 1)
@@ -262,9 +305,7 @@ def main():
     ssd.timer_enable(0)
     ms = start.elapsed_time(stop) / a.steps
     ms_sep = s0.elapsed_time(s1) / a.steps
-    t_s = ev[0].elapsed_time(ev[1]) / a.steps
-    t_v = ev[1].elapsed_time(ev[2]) / a.steps
-    t_ve = ev[2].elapsed_time(ev[3]) / a.steps
+    t_s, t_v, t_ve = (sum(x) / len(x) for x in call_ms)
     acc = acc_buf[a.warmup:].to(torch.int64)
     tokens = int((acc + 1).sum().item())
     # residual row pairs per step: T > 0 sequences with k* < K
