@@ -865,25 +865,28 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
   const int64_t rs = p.ld * Dt<DT>::SZ;
   const bool lead = chunk == 0;
   // wave 0, lane j < K: drafted token, sigma_j(x_j), the target logit at x_j
-  // captured by the streaming pass; lane j <= K: the draft row statistics
-  int xj = -1;
-  float qj = 0.f, ztj = 0.f, dmax = 0.f;
-  double dlse = 0.0;
-  if (tid < K) {
-    xj = p.dtok[b * K + tid];
-    qj = p.dq[b * K + tid];
-    ztj = p.zcap[b * K + tid];
-  }
-  if (tid <= K && !greedy) {
-    const ssd_row_stats ds = p.dstats[r0 + tid];
-    dmax = ds.max;
-    dlse = ds.lse;
-  }
-  // the draft top-F lists of all K + 1 rows (the residual of row k* needs
-  // one), fetched with the rest so that no load waits on k*
+  // captured by the streaming pass; lane j <= K: the draft row statistics;
+  // thread t < (K+1) F: entry t of the draft top-F lists of all K + 1 rows
+  // (the residual of row k* needs one).  All loaded unconditionally from
+  // clamped indices (a valid stand-in array when K = 0 or F = 0: the
+  // captured-logit workspace), so that they and the partials below are in
+  // flight together (a load under a branch gets a wait of its own) and no
+  // load waits on k*.
   const int F = p.F;
   const bool tf_lds = F > 0 && K1 * F <= TF_CAP;
-  if (tf_lds && tid < K1 * F) sm.tf[tid] = p.dtopf[(r0 + tid / F) * p.ld_dtopf + tid % F];
+  const int tq = min(tid, max(K - 1, 0));
+  const int32_t* dtok = K > 0 ? p.dtok : reinterpret_cast<const int32_t*>(p.zcap);
+  const float* dqp = K > 0 ? p.dq : p.zcap;
+  const int xl = dtok[b * K + tq];
+  const float ql = dqp[b * K + tq], zl = p.zcap[b * K + tq];
+  const ssd_row_stats ds = p.dstats[r0 + min(tid, K)];
+  const int tt = tf_lds ? min(tid, K1 * F - 1) : 0;
+  const int32_t* tfp = tf_lds ? p.dtopf + (r0 + tt / F) * p.ld_dtopf + tt % F : reinterpret_cast<const int32_t*>(p.zcap);
+  const int tfv = *tfp;
+  const int xj = tid < K ? xl : -1;
+  const float qj = tid < K ? ql : 0.f, ztj = tid < K ? zl : 0.f;
+  const float dmax = (tid <= K && !greedy) ? ds.max : 0.f;
+  const double dlse = (tid <= K && !greedy) ? (double)ds.lse : 0.0;
   // row statistics: wave w merges rows j = w, w + ENW, ..., two rows per pass
   // with both rows' loads in flight
   auto merge = [&](const WRow<PLN>& r, int j) {
@@ -932,6 +935,7 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     merge(ra, j0);
     if (j1 < K1) merge(rb, j1);
   }
+  if (tf_lds && tid < K1 * F) sm.tf[tid] = tfv;
   __syncthreads();
   // argmax of the T > 0 rows is only needed for the optional statistics
   if (lead && !greedy && p.stats) {
