@@ -188,6 +188,7 @@ EARLY = [
     (8, 7, 40000, BF16, 1.0, 4, 0.5, "zipf", False, 8),     # J = K + 1: every row up front
     (5, 2, 300000, BF16, 1.0, 4, 0.5, "zipf", False, 2),    # NB > 128
     (2, 0, 3000, BF16, 1.0, 2, 0.5, "normal", False, 1),    # K = 0
+    (4, 3, 4099, F16, 1.1, 0, 1.0, "normal", True, 2),      # unaligned fp16, F = 0, C = 1, greedy half
 ]
 
 
