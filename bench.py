@@ -26,10 +26,9 @@ with the library's kernel timer on, which stamps the streaming launches
 with HIP events recorded by the launch itself on the call's stream; each of
 those loops is then captured in a HIP graph and replayed (every replay
 checked against the eager results) for the per-call times ms_sample,
-ms_verify and ms_verify_early, free of the Python binding's host path.  The
-headline schedule runs once more with the timer, right after the headline
-pass, for the shared launch (separate passes, because the event work slows
-the step).  Algorithmic bytes: B (K+1) V element bytes read + one
+ms_verify and ms_verify_early, free of the Python binding's host path; the
+headline schedule runs once more with the timer for the shared launch
+(separate passes, because the event work slows the step).  Algorithmic bytes: B (K+1) V element bytes read + one
 16-byte partial per 2048-token block written, + for the shared launch the
 draft row k* of every sequence with a residual and the residual block sums
 (+ for the verification stream the drafted tokens and captured logits).
@@ -217,14 +216,6 @@ def main():
     same = bool(torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:]))
     if not same:
         raise SystemExit("ssd_round gave other accepted lengths or cache hits than the separate calls")
-    # the headline schedule once more with the kernel timer, right after the
-    # headline pass (same conditions): there the sampling op is the shared
-    # launch (sampling stream + residual pass)
-    ssd.timer_enable(a.steps + 1)
-    run_rounds(a.warmup, total)
-    torch.cuda.synchronize()
-    r_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
-    ssd.timer_enable(0)
     # per-call pass: each entry point over all the timed steps back to back
     # (the host enqueues ahead, so the times are the GPU's), with per-step
     # sampling outputs and cache keys, and the streaming launches stamped by
@@ -305,6 +296,13 @@ def main():
             call_ms[k].append(e0.elapsed_time(e1) / a.steps)
         if not results_match():
             raise SystemExit(f"graph replay {rep_} gave other accepted lengths or cache hits")
+    # and the headline schedule once more with the timer: there the sampling
+    # op is the shared launch (sampling stream + residual pass)
+    ssd.timer_enable(a.steps + 1)
+    run_rounds(a.warmup, total)
+    torch.cuda.synchronize()
+    r_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
+    ssd.timer_enable(0)
     ms = start.elapsed_time(stop) / a.steps
     ms_sep = s0.elapsed_time(s1) / a.steps
     t_s, t_v, t_ve = (sum(x) / len(x) for x in call_ms)
