@@ -144,7 +144,9 @@ struct RawBlock {
   uint32_t w[N];
 };
 
-template <int DT, bool AL, bool FULL>
+// NT: full blocks are read with the nontemporal hint (the default: each logit
+// is read once), or with ordinary loads for rows a later kernel may re-read.
+template <int DT, bool AL, bool FULL, bool NT = true>
 __device__ __forceinline__ void load_raw(const unsigned char* row, int V, int beta, int lane, RawBlock<DT, AL>& r) {
   constexpr int VW = Dt<DT>::VW;
   const int base = beta * BLK + lane * VW;
@@ -153,7 +155,8 @@ __device__ __forceinline__ void load_raw(const unsigned char* row, int V, int be
     for (int i = 0; i < 32 / VW; ++i) {
       const int e0 = base + i * 64 * VW;
       if constexpr (FULL) {
-        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + (size_t)e0 * Dt<DT>::SZ));
+        const u32x4* ptr = reinterpret_cast<const u32x4*>(row + (size_t)e0 * Dt<DT>::SZ);
+        const u32x4 t = NT ? __builtin_nontemporal_load(ptr) : *ptr;
         r.w[4 * i] = t.x; r.w[4 * i + 1] = t.y; r.w[4 * i + 2] = t.z; r.w[4 * i + 3] = t.w;
       } else {
         const bool in = e0 < V;

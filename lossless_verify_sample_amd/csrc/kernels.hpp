@@ -58,6 +58,7 @@ struct Params {
   int racc;                 // verification: blocks per workgroup of the residual pass (a multiple of CH_R)
   int jlo, jn;              // jn > 0: the streaming pass covers positions jlo .. jlo + jn - 1 of every sequence
   int early;                // verification: rows past the first rejection may not have been streamed
+  int keep;                 // verification: positions < keep are streamed with ordinary (cached) loads
   int K, B;
   const float* temp;
   int F, F_out, F_sel;
@@ -1178,7 +1179,14 @@ __device__ __forceinline__ void stream_item(const Params& p, int item) {
   // token) are fetched behind them
   RawBlock<DT, AL> r0, r1;
   const bool full = (chunk + 1) * CH * BLK <= V;
-  if (full) {
+  // verification: the first p.keep target rows of a sequence, the likeliest
+  // rows of the first rejection, are read with ordinary loads so that the
+  // residual pass's re-read of row k* may find them in the Infinity Cache
+  const bool keep = MODE == M_VERIFY && (int)(row % K1) < p.keep;
+  if (full && keep) {
+    load_raw<DT, AL, true, false>(rp, V, b0, lane, r0);
+    load_raw<DT, AL, true, false>(rp, V, b1, lane, r1);
+  } else if (full) {
     // every block of this chunk is full: all loads in flight together
     load_raw<DT, AL, true>(rp, V, b0, lane, r0);
     load_raw<DT, AL, true>(rp, V, b1, lane, r1);
