@@ -284,7 +284,8 @@ def main():
     for rep_ in range(3):
         acc_buf[a.warmup:].fill_(-1)
         acc_early.fill_(-1)
-        hit_buf[a.warmup:].fill_(-1)
+        if use_cache:  # (written only by the cache lookup)
+            hit_buf[a.warmup:].fill_(-1)
         torch.cuda.synchronize()
         for k, g in enumerate(graphs):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
