@@ -95,8 +95,9 @@ class Cache:
                 if tuple(self.payload.shape) != (self.B, self.Bgt, self.K):
                     raise SSDError("cache payload must be [B, Bgt, K]")
                 st.payload = _p(self.payload)
-            for t, n in ((self.hit, "hit"), (self.slot, "slot"), (self.tokens, "tokens")):
-                _need(t, torch.int32, "cache " + n, dev)
+            for t, n, shp in ((self.hit, "hit", (self.B,)), (self.slot, "slot", (self.B,)),
+                              (self.tokens, "tokens", (self.B, self.K))):
+                _shaped(t, torch.int32, shp, "cache " + n, dev)
             st.out_hit, st.out_slot, st.out_tokens = _p(self.hit), _p(self.slot), _p(self.tokens)
             st.miss_fill = 1 if self.miss_fill else 0
         return st
@@ -177,6 +178,22 @@ def _need(t, dtype, name, dev=None):
         raise SSDError(f"{name} is on {t.device}, expected {dev}")
     if not t.is_contiguous():
         raise SSDError(f"{name} must be contiguous")
+
+
+def _shaped(t, dtype, shape, name, dev):
+    """A device tensor of `dtype`, contiguous, of exactly `shape` (the
+    kernels index it by B, K and the list widths with no bounds of their
+    own)."""
+    _need(t, dtype, name, dev)
+    if tuple(t.shape) != tuple(shape):
+        raise SSDError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stats_shaped(t, n, name, dev):
+    """ssd_row_stats [n] as a contiguous float64 tensor of 2 n elements."""
+    _need(t, torch.float64, name, dev)
+    if t.numel() != 2 * n:
+        raise SSDError(f"{name} must hold {n} row statistics ({2 * n} float64), got {t.numel()}")
 
 
 def _rows_ld(x, nd):
@@ -288,6 +305,15 @@ def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=N
                    stats=_stats_tensor(B * K1, dev),
                    topf_idx=torch.empty((B, K1, F_out), dtype=torch.int32, device=dev),
                    topf_val=torch.empty((B, K1, F_out), dtype=torch.float32, device=dev))
+    _shaped(out["tokens"], torch.int32, (B, K), "tokens", dev)
+    _shaped(out["q"], torch.float32, (B, K), "q", dev)
+    _stats_shaped(out["stats"], B * K1, "stats", dev)
+    if F_out > 0:
+        _shaped(out["topf_idx"], torch.int32, (B, K1, F_out), "topf_idx", dev)
+        if out.get("topf_val") is not None:
+            _shaped(out["topf_val"], torch.float32, (B, K1, F_out), "topf_val", dev)
+    if cache is not None and (cache.B, cache.K) != (B, K):
+        raise SSDError("the cache was made for another batch size or K")
     ws = _workspace(OP_SAMPLE, B, K, V, dev)
     cs = cache._struct(dev, False) if cache is not None else None
     args = (_p(draft), _DT[draft.dtype], B, K, V, ld, _p(temperature), F, float(C), F_out, int(seed) & (2 ** 64 - 1),
@@ -314,18 +340,30 @@ def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats,
     K = K1 - 1
     dev = target.device
     _need(temperature, torch.float32, "temperature", dev)
-    _need(tokens, torch.int32, "tokens", dev)
-    _need(draft_q, torch.float32, "draft_q", dev)
-    _need(draft_stats, torch.float64, "draft_stats", dev)
+    if temperature.numel() != B:
+        raise SSDError("temperature must have one entry per sequence")
+    _shaped(tokens, torch.int32, (B, K), "tokens", dev)
+    _shaped(draft_q, torch.float32, (B, K), "draft_q", dev)
+    _stats_shaped(draft_stats, B * K1, "draft_stats", dev)
     ldf = 0
     if F > 0:
         _need(draft_topf_idx, torch.int32, "draft_topf_idx", dev)
+        if draft_topf_idx.dim() != 3 or tuple(draft_topf_idx.shape[:2]) != (B, K1) or draft_topf_idx.shape[2] < F:
+            raise SSDError(f"draft_topf_idx must be [B, K+1, >= F] = [{B}, {K1}, >= {F}], "
+                           f"got {tuple(draft_topf_idx.shape)}")
         ldf = draft_topf_idx.shape[-1]
     if out is None:
         out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
                    bonus=torch.empty(B, dtype=torch.int32, device=dev),
                    p=torch.empty((B, K), dtype=torch.float32, device=dev),
                    stats=_stats_tensor(B * K1, dev) if want_stats else None)
+    _shaped(out["accept_len"], torch.int32, (B,), "accept_len", dev)
+    _shaped(out["bonus"], torch.int32, (B,), "bonus", dev)
+    _shaped(out["p"], torch.float32, (B, K), "p", dev)
+    if out.get("stats") is not None:
+        _stats_shaped(out["stats"], B * K1, "stats", dev)
+    if cache is not None and (cache.B, cache.K) != (B, K):
+        raise SSDError("the cache was made for another batch size or K")
     ws = _workspace(OP_VERIFY, B, K, V, dev)
     cs = cache._struct(dev, True) if cache is not None else None
     args = (_p(target), _p(draft), _DT[target.dtype], B, K, V, ld, _p(temperature), F, float(C),
@@ -387,7 +425,11 @@ def cache_keys(topf_idx, depth_off, Bgt):
     _need(topf_idx, torch.int32, "topf_idx")
     dev = topf_idx.device
     _need(depth_off, torch.int32, "depth_off", dev)
+    if topf_idx.dim() != 3:
+        raise SSDError("topf_idx must be [B, K+1, ldf]")
     B, K1, ldf = topf_idx.shape
+    if depth_off.numel() != K1 + 1:
+        raise SSDError("depth_off must have K+2 entries")
     keys = torch.empty((B, Bgt), dtype=torch.int32, device=dev)
     _check(_lib.ssd_cache_keys(_p(topf_idx), ldf, _p(depth_off), B, K1 - 1, Bgt, _p(keys), _stream(dev)),
            "ssd_cache_keys")
@@ -401,10 +443,14 @@ def cache_lookup(keys, depth_off, payload, accept_len, bonus, miss_fill=False, V
     dev = keys.device
     for t, n in ((depth_off, "depth_off"), (payload, "payload"), (accept_len, "accept_len"), (bonus, "bonus")):
         _need(t, torch.int32, n, dev)
+    if keys.dim() != 2 or payload.dim() != 3:
+        raise SSDError("keys must be [B, Bgt] and payload [B, Bgt, K]")
     B, Bgt = keys.shape
     K = payload.shape[2]
     if payload.shape[:2] != (B, Bgt) or depth_off.numel() != K + 2:
         raise SSDError("payload must be [B, Bgt, K] and depth_off [K+2]")
+    if accept_len.numel() != B or bonus.numel() != B:
+        raise SSDError("accept_len and bonus must have one entry per sequence")
     hit = torch.empty(B, dtype=torch.int32, device=dev)
     slot = torch.empty(B, dtype=torch.int32, device=dev)
     toks = torch.empty((B, K), dtype=torch.int32, device=dev)

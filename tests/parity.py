@@ -35,6 +35,7 @@ def raw_host(x):
 class Report:
     units: int = 0
     near: int = 0
+    hits: int = 0
     fails: list = field(default_factory=list)
 
     def fail(self, msg):
@@ -125,12 +126,14 @@ def compare_verify(rep, g, o, T):
         compare_stats(rep, "target", g["stats"], o["max"], o["lse"], o["argmax"], greedy)
 
 
-def gpu_round(target, draft, T, F, C, seed, F_out=None):
-    """One sample + verify on the GPU; numpy copies of every output."""
+def gpu_round(target, draft, T, F, C, seed, F_out=None, cache=None):
+    """One sample + verify on the GPU (with a speculation cache when given:
+    sampling writes its keys, verification looks the outcome up); numpy
+    copies of every output."""
     B, K1, V = draft.shape
-    smp = ssd.saguaro_sample(draft, T, F, C, seed, F_out=F_out)
+    smp = ssd.saguaro_sample(draft, T, F, C, seed, F_out=F_out, cache=cache)
     ver = ssd.verify(target, draft, T, F, C, seed, smp["tokens"], smp["q"], smp["stats"], smp["topf_idx"],
-                     want_stats=True)
+                     want_stats=True, cache=cache)
     torch.cuda.synchronize()
     g_s = dict(tokens=smp["tokens"].cpu().numpy(), q=smp["q"].cpu().numpy().astype(np.float64),
                stats=stats_np(smp["stats"], B, K1), topf_idx=smp["topf_idx"].cpu().numpy(),
@@ -140,15 +143,41 @@ def gpu_round(target, draft, T, F, C, seed, F_out=None):
     return g_s, g_v, smp, ver
 
 
-def check_round(target, draft, T, F, C, seed, F_out=None, workers=None):
+def check_round(target, draft, T, F, C, seed, F_out=None, workers=None, pool=None, cache=None):
     """GPU sample + verify against the oracle on the same inputs.  The oracle
-    verifies the GPU's drafted tokens so later units stay comparable."""
-    g_s, g_v, smp, ver = gpu_round(target, draft, T, F, C, seed, F_out)
+    verifies the GPU's drafted tokens so later units stay comparable.  With a
+    cache, the keys sampling wrote are checked against the oracle's top
+    lists and the lookup against the oracle's lookup of the GPU's (k*,
+    bonus), which are themselves checked against the oracle's."""
+    g_s, g_v, smp, ver = gpu_round(target, draft, T, F, C, seed, F_out, cache)
     Th = T.cpu().numpy().astype(np.float64)
     dt = DTNAME[draft.dtype]
-    o = OP.run(raw_host(draft), dt, Th, F, C, seed, F_out=F_out if F_out is not None else F,
-               target_raw=raw_host(target), tokens=g_s["tokens"].astype(np.int64), workers=workers)
+    fo = F_out if F_out is not None else F
+    fl = max(fo, max(cache.fanout)) if cache is not None else fo
+    o = OP.run(raw_host(draft), dt, Th, F, C, seed, F_out=fl, target_raw=raw_host(target),
+               tokens=g_s["tokens"].astype(np.int64), workers=workers, pool=pool)
     rep = Report()
-    compare_draft(rep, g_s, o["draft"], Th)
+    od = dict(o["draft"], topf_idx=o["draft"]["topf_idx"][:, :, :fo], topf_val=o["draft"]["topf_val"][:, :, :fo])
+    compare_draft(rep, g_s, od, Th)
     compare_verify(rep, g_v, o["verify"], Th)
+    if cache is not None:
+        compare_cache(rep, cache, o["draft"]["topf_idx"], g_v, seed, draft.shape[2])
     return rep, g_s, g_v, smp, ver, o
+
+
+def compare_cache(rep, cache, o_lists, g_v, seed, V):
+    """Keys [B, Bgt] against the first F_k entries of the oracle's top lists
+    of each draft row; hit, slot and gathered (or filled) tokens against the
+    oracle's lookup of the GPU's accepted lengths and bonus tokens."""
+    keys_o, off = O.build_keys(o_lists, cache.fanout)
+    keys = cache.keys.cpu().numpy()
+    if not np.array_equal(keys, keys_o):
+        bad = np.argwhere(keys != keys_o)[:3]
+        rep.fail(f"cache keys differ at {bad.tolist()}")
+    pay = cache.payload.cpu().numpy() if cache.payload is not None else np.zeros((keys.shape[0], cache.Bgt, 0))
+    oh, osl, ot = O.cache_lookup(keys_o, off, pay, g_v["accept_len"], g_v["bonus"], seed=seed, V=V,
+                                 miss_fill=cache.miss_fill)
+    for name, g, o in (("hit", cache.hit, oh), ("slot", cache.slot, osl), ("tokens", cache.tokens, ot)):
+        if not np.array_equal(g.cpu().numpy(), o):
+            rep.fail(f"cache {name} differs")
+    rep.hits = int(oh.sum())

@@ -252,23 +252,6 @@ def test_verify_early_full_size(c, J):
          f"{int((acc >= J).sum())} of {cfg.B} (at least)")
 
 
-@pytest.mark.parametrize("c", [2, 3, 4, 5])
-def test_full_size_workload(c):
-    cfg = W.CONFIGS[c]
-    rep = Report()
-    for step in range(2):
-        _say(f"config {c} ({cfg.name}) step {step}: B={cfg.B} K={cfg.K} V={cfg.V}")
-        t, d = W.logits(cfg, step, DEV)
-        r, g_s, g_v, smp, ver, o = check_round(t, d, W.temperatures(cfg, DEV), cfg.F, cfg.C,
-                                               W.seed(cfg, step), F_out=cfg.fout)
-        rep.add(r)
-        _say(f"  units {r.units} near {r.near} fails {len(r.fails)} "
-             f"mean k* {g_v['accept_len'].mean():.3f}")
-        del t, d
-    assert rep.ok(), rep.fails
-    assert rep.near < 1e-4 * rep.units, (rep.near, rep.units)
-
-
 def test_cache_lookup_against_oracle():
     import lossless_verify_sample_amd as ssd
     from oracle import ssd as O
@@ -411,3 +394,90 @@ def test_round_step_matches_separate_calls(case):
     for a, b in zip(c_got, c_ref):
         assert torch.equal(a, b)
     _say(f"round {case[:3]}: accepted {v_ref['accept_len'].tolist()} hits {c_ref[0].tolist()}")
+
+
+FBIG = [
+    # B, K, V, dtype, T, F, C, F_out, kind, greedy_half: sigma over F > 8 entries (the radix
+    # threshold), and (K+1) F > 256, where acceptance, residual and bonus read the draft top-F
+    # lists from global memory instead of LDS
+    (3, 7, 151936, BF16, 1.0, 16, 0.5, 16, "zipf", False),   # (K+1) F = 128
+    (3, 7, 151936, BF16, 1.0, 40, 0.4, 40, "zipf", False),   # (K+1) F = 320
+    (2, 3, 151936, BF16, 0.8, 64, 0.3, 64, "peaks", False),  # (K+1) F = 256, the LDS limit
+    (4, 4, 151936, F16, 1.0, 64, 0.5, 64, "zipf", True),     # (K+1) F = 320, greedy half
+    (3, 7, 40001, F32, 1.1, 40, 0.5, 40, "normal", False),   # unaligned fp32; 2 NB = F: exact fallback
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", FBIG, ids=lambda c: f"B{c[0]}K{c[1]}V{c[2]}{DTNAME[c[3]]}F{c[5]}")
+def test_large_f(case):
+    """sigma_{F,C} with F in {16, 40, 64} through ssd_saguaro_sample and
+    ssd_verify against the oracle, ssd_verify_early against both, and
+    ssd_round against the separate calls."""
+    B, K, V, dt, T, F, C, Fo, kind, gh = case
+    cfg = W.custom(B, K, V, dt, T=T, F=F, C=C, kind=kind, draft_sd=0.8, F_out=Fo, greedy_half=gh)
+    temp = W.temperatures(cfg, DEV)
+    rep = Report()
+    for step in range(3):
+        _say(f"large F {cfg.name} F={F} step {step}")
+        t, d = W.logits(cfg, step, DEV)
+        r, *_ = check_round(t, d, temp, F, C, W.seed(cfg, step), F_out=Fo)
+        rep.add(r)
+        _check_early(t, d, temp, F, C, W.seed(cfg, step), 2, F_out=Fo)
+    assert rep.ok(), rep.fails
+    # the pipeline step: every output as the separate calls give it
+    t, d = W.logits(cfg, 10, DEV)
+    _, d1 = W.logits(cfg, 11, DEV)
+    s0 = ssd.saguaro_sample(d, temp, F, C, 5, F_out=Fo)
+
+    def run(use_round):
+        va = dict(target=t, draft=d, temperature=temp, F=F, C=C, seed=5, tokens=s0["tokens"], draft_q=s0["q"],
+                  draft_stats=s0["stats"], draft_topf_idx=s0["topf_idx"], want_stats=True)
+        sa = dict(draft=d1, temperature=temp, F=F, C=C, seed=6, F_out=Fo)
+        v, s = ssd.round_step(va, sa) if use_round else (ssd.verify(**va), ssd.saguaro_sample(**sa))
+        torch.cuda.synchronize()
+        return {k: x.clone() for k, x in v.items()}, {k: x.clone() for k, x in s.items()}
+
+    v_ref, s_ref = run(False)
+    v_got, s_got = run(True)
+    for k in v_ref:
+        assert torch.equal(v_got[k], v_ref[k]), k
+    for k in s_ref:
+        assert torch.equal(s_got[k], s_ref[k]), k
+    _say(f"large F {cfg.name}: units {rep.units} near {rep.near}")
+
+
+def test_binding_rejects_misshaped_tensors():
+    """The binding checks every tensor the kernels index by B, K and the list
+    widths, and raises before calling the library."""
+    B, K, V = 3, 4, 5000
+    cfg = W.custom(B, K, V, BF16)
+    t, d = W.logits(cfg, 0, DEV)
+    T = W.temperatures(cfg, DEV)
+    s = ssd.saguaro_sample(d, T, 4, 0.5, 1)
+    good = dict(tokens=s["tokens"], draft_q=s["q"], draft_stats=s["stats"], draft_topf_idx=s["topf_idx"])
+    bad = [dict(tokens=s["tokens"][:, :2].contiguous()), dict(draft_q=torch.ones((B + 1, K), device=DEV)),
+           dict(draft_stats=s["stats"][:-1].contiguous()), dict(draft_topf_idx=s["topf_idx"][:, :, :2].contiguous()),
+           dict(draft_topf_idx=s["topf_idx"][:2].contiguous())]
+    for kw in bad:
+        with pytest.raises(ssd.SSDError):
+            ssd.verify(t, d, T, 4, 0.5, 1, **dict(good, **kw))
+    with pytest.raises(ssd.SSDError):
+        ssd.verify(t, d, T, 4, 0.5, 1, **good, out=dict(accept_len=torch.empty(B + 1, dtype=torch.int32, device=DEV),
+                                                        bonus=torch.empty(B, dtype=torch.int32, device=DEV),
+                                                        p=torch.empty((B, K), device=DEV)))
+    with pytest.raises(ssd.SSDError):
+        ssd.saguaro_sample(d, T, 4, 0.5, 1, out=dict(s, q=torch.empty((B, K + 1), device=DEV)))
+    with pytest.raises(ssd.SSDError):
+        ssd.saguaro_sample(d, T, 4, 0.5, 1, F_out=6, out=s)  # lists of 4 for F_out = 6
+    c = ssd.Cache([2] * (K + 1), B, K, DEV, payload=W.payload(cfg, 2 * (K + 1), 0, DEV))
+    c.tokens = torch.empty((B, K - 1), dtype=torch.int32, device=DEV)
+    with pytest.raises(ssd.SSDError):
+        ssd.verify(t, d, T, 4, 0.5, 1, **good, cache=c)
+    keys = torch.zeros((B, 10), dtype=torch.int32, device=DEV)
+    off = torch.tensor([0, 2, 4, 6, 8, 10], dtype=torch.int32, device=DEV)
+    pay = torch.zeros((B, 10, K), dtype=torch.int32, device=DEV)
+    with pytest.raises(ssd.SSDError):
+        ssd.cache_lookup(keys, off, pay, torch.zeros(B - 1, dtype=torch.int32, device=DEV),
+                         torch.zeros(B, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
