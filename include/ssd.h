@@ -24,7 +24,8 @@
  *   entry.  NaN and +inf are not supported.
  * - Pointers named "device" are HIP device memory owned by the caller; the
  *   library allocates no device memory and keeps no state between calls
- *   (the optional kernel timer below aside).
+ *   (the optional kernel timer below and the static scratch of
+ *   ssd_round_noalloc aside).
  * - `stream` is a hipStream_t (NULL = default stream).  Every call is
  *   asynchronous: it validates its scalar arguments, enqueues its kernels
  *   and returns; nothing synchronises inside the library.
@@ -75,7 +76,9 @@ typedef enum {
   SSD_ERR_INVALID_ARG = 1, /* null pointer, size out of range, bad C, ... */
   SSD_ERR_UNSUPPORTED = 2, /* valid request this build does not handle   */
   SSD_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned */
-  SSD_ERR_HIP = 4          /* a HIP launch failed                        */
+  SSD_ERR_HIP = 4,         /* a HIP launch failed                        */
+  SSD_ERR_SCRATCH_LIMIT = 5 /* ssd_round_noalloc: the request needs more than
+                               the library's static scratch               */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 } ssd_dtype;
@@ -294,6 +297,26 @@ ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream);
  * (tokens, q, stats, top-F indices) is the verification's input of the same
  * kind or both use the same cache keys (other aliasing is not detected). */
 ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream);
+
+/* ssd_round for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, checks and results as ssd_round, except that the
+ * `workspace` and `ws_bytes` fields of v and s are ignored (they may be NULL
+ * and 0).  The kernels use instead a scratch array the library holds in
+ * device memory, SSD_NOALLOC_HALF_BYTES for the verification and as much for
+ * the sampling, on every GPU it runs on, until the process ends; this call
+ * allocates nothing.  The caller still passes every input and output.
+ * The scratch needs no initialisation (every region is written before it is
+ * read within a call) and keeps the last call's contents.  All calls of this
+ * entry point on one GPU share that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give undefined results.
+ * The device is the stream's (the current device for a NULL stream); its
+ * scratch address is looked up on the first call there.
+ * Errors: as ssd_round; SSD_ERR_SCRATCH_LIMIT when either call needs more
+ * than SSD_NOALLOC_HALF_BYTES (ssd_workspace_bytes of its op; about 1 KB per
+ * logit row and 2048 vocabulary entries), before any launch. */
+#define SSD_NOALLOC_HALF_BYTES (8u << 20)
+ssd_status ssd_round_noalloc(const ssd_verify_args* v, const ssd_sample_args* s, void* stream);
 
 /* Speculation-cache lookup keyed by (accepted length, bonus token) ([SSD-B]
  * core-mechanism section: the draft builds a speculation cache while the

@@ -117,6 +117,7 @@ def _load():
         "ssd_cache_lookup": [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _u64, _vp],
         "ssd_backoff": [_vp, _i32, _vp, _vp, _vp],
         "ssd_round": [_vp, _vp, _vp],
+        "ssd_round_noalloc": [_vp, _vp, _vp],
         "ssd_verify_early": [_vp, _i32, _vp],
         "ssd_fanout_greedy": [_vp, _vp, _i32, _i32, _i32, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
@@ -284,7 +285,7 @@ def topf(logits, F):
     return idx, val
 
 
-def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=None, _defer=None):
+def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=None, _defer=None, _ws=True):
     """Draft sampling with sigma_{F,C} over draft logits [B, K+1, V].
 
     Returns dict(tokens [B,K] int32, q [B,K] f32, stats [B*(K+1), 2] (see
@@ -314,11 +315,11 @@ def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=N
             _shaped(out["topf_val"], torch.float32, (B, K1, F_out), "topf_val", dev)
     if cache is not None and (cache.B, cache.K) != (B, K):
         raise SSDError("the cache was made for another batch size or K")
-    ws = _workspace(OP_SAMPLE, B, K, V, dev)
+    ws = _workspace(OP_SAMPLE, B, K, V, dev) if _ws else None
     cs = cache._struct(dev, False) if cache is not None else None
     args = (_p(draft), _DT[draft.dtype], B, K, V, ld, _p(temperature), F, float(C), F_out, int(seed) & (2 ** 64 - 1),
             _p(out["tokens"]), _p(out["q"]), _p(out["stats"]), _p(out["topf_idx"]), _p(out["topf_val"]),
-            ctypes.cast(ctypes.pointer(cs), _vp) if cs is not None else None, _p(ws), ws.numel())
+            ctypes.cast(ctypes.pointer(cs), _vp) if cs is not None else None, _p(ws), ws.numel() if _ws else 0)
     if _defer is not None:
         _defer.extend([cs])
         return out, args
@@ -327,7 +328,7 @@ def saguaro_sample(draft, temperature, F, C, seed, F_out=None, out=None, cache=N
 
 
 def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats, draft_topf_idx, want_stats=False,
-           out=None, cache=None, _defer=None):
+           out=None, cache=None, _defer=None, _ws=True):
     """Acceptance test, accepted length and bonus for target/draft [B, K+1, V].
 
     Returns dict(accept_len [B] int32, bonus [B] int32, p [B,K] f32, stats
@@ -364,13 +365,13 @@ def verify(target, draft, temperature, F, C, seed, tokens, draft_q, draft_stats,
         _stats_shaped(out["stats"], B * K1, "stats", dev)
     if cache is not None and (cache.B, cache.K) != (B, K):
         raise SSDError("the cache was made for another batch size or K")
-    ws = _workspace(OP_VERIFY, B, K, V, dev)
+    ws = _workspace(OP_VERIFY, B, K, V, dev) if _ws else None
     cs = cache._struct(dev, True) if cache is not None else None
     args = (_p(target), _p(draft), _DT[target.dtype], B, K, V, ld, _p(temperature), F, float(C),
             int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_q), _p(draft_stats),
             _p(draft_topf_idx) if F > 0 else None, ldf, _p(out["accept_len"]), _p(out["bonus"]),
             _p(out["p"]), _p(out.get("stats")), ctypes.cast(ctypes.pointer(cs), _vp) if cs is not None else None,
-            _p(ws), ws.numel())
+            _p(ws), ws.numel() if _ws else 0)
     if _defer is not None:
         _defer.extend([cs])
         return out, args
@@ -396,27 +397,31 @@ def verify_early(target, draft, temperature, F, C, seed, tokens, draft_q, draft_
     return o
 
 
-def round_step(verify_args=None, sample_args=None):
+def round_step(verify_args=None, sample_args=None, noalloc=False):
     """One pipeline step (ssd_round): verification of round i and draft
     sampling of round i + 1, each given as a dict of the keyword arguments of
     verify() / saguaro_sample() (with their positional ones under the same
     names).  Results are those of verify(...) then saguaro_sample(...); the
-    sampling's outputs must not be the verification's inputs.  Returns
-    (verify outputs or None, sample outputs or None)."""
+    sampling's outputs must not be the verification's inputs.  With
+    noalloc=True the step runs through ssd_round_noalloc on the library's own
+    scratch (no workspace is passed; outputs the caller does not give are
+    still allocated here).  Returns (verify outputs or None, sample outputs
+    or None)."""
     keep = []
     vo = so = None
     vs = ss = None
     if verify_args is not None:
-        vo, a = verify(**verify_args, _defer=keep)
+        vo, a = verify(**verify_args, _defer=keep, _ws=not noalloc)
         vs = _VerifyArgs(*a)
     if sample_args is not None:
-        so, a = saguaro_sample(**sample_args, _defer=keep)
+        so, a = saguaro_sample(**sample_args, _defer=keep, _ws=not noalloc)
         ss = _SampleArgs(*a)
     if vs is None and ss is None:
         raise SSDError("round_step needs a verification or a sampling")
     dev = (verify_args["target"] if verify_args is not None else sample_args["draft"]).device
-    _check(_lib.ssd_round(ctypes.byref(vs) if vs is not None else None, ctypes.byref(ss) if ss is not None else None,
-                          _stream(dev)), "ssd_round")
+    fn, name = (_lib.ssd_round_noalloc, "ssd_round_noalloc") if noalloc else (_lib.ssd_round, "ssd_round")
+    _check(fn(ctypes.byref(vs) if vs is not None else None, ctypes.byref(ss) if ss is not None else None,
+              _stream(dev)), name)
     return vo, so
 
 

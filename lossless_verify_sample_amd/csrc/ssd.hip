@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include <hip/hip_ext.h>
@@ -13,6 +14,13 @@
 #include "kernels.hpp"
 
 using namespace ssd;
+
+// Library-owned scratch for ssd_round_noalloc (callers that cannot allocate
+// device memory): the verification's workspace in the first half, the
+// sampling's in the second.  Each GPU the library runs on holds its own copy
+// until the process ends.
+constexpr size_t kScratchHalf = SSD_NOALLOC_HALF_BYTES;
+static __device__ __align__(256) unsigned char scratch[2 * kScratchHalf];
 
 namespace {
 
@@ -321,6 +329,96 @@ hipError_t launch_verify(const Plan& q, hipStream_t st) {
   return e;
 }
 
+// The two calls of a pipeline step, checked (see ssd_round).
+ssd_status plan_round(const ssd_verify_args* v, const ssd_sample_args* s, Plan& qv, Plan& qs) {
+  if (!v && !s) return SSD_ERR_INVALID_ARG;
+  if (v) {
+    const ssd_status e = plan_verify(*v, qv);
+    if (e != SSD_OK) return e;
+  }
+  if (s) {
+    const ssd_status e = plan_sample(*s, qs);
+    if (e != SSD_OK) return e;
+  }
+  if (v && s && (v->workspace == s->workspace)) return SSD_ERR_WORKSPACE;
+  if (v && s) {
+    // round i+1's sampling must not write what round i's verification reads
+    const void* w[] = {s->out_tokens, s->out_q, s->out_stats, s->out_topf_idx};
+    const void* r[] = {v->draft_tokens, v->draft_q, v->draft_stats, v->draft_topf_idx};
+    for (const void* a : w)
+      for (const void* b : r)
+        if (a && a == b) return SSD_ERR_INVALID_ARG;
+    if (v->cache && s->cache && v->cache->keys && v->cache->keys == s->cache->keys) return SSD_ERR_INVALID_ARG;
+  }
+  return SSD_OK;
+}
+
+// Launches of a planned pipeline step (either plan may be absent).
+ssd_status launch_round(const Plan* pqv, const Plan* pqs, hipStream_t st) {
+  (void)hipGetLastError();
+  if (!pqv) return hip_status(launch_sample(*pqs, st));
+  if (!pqs) return hip_status(launch_verify(*pqv, st));
+  const Plan& qv = *pqv;
+  const Plan& qs = *pqs;
+  if (qv.dt != qs.dt || qv.al != qs.al) {
+    // kernels of different element types cannot share a launch: in turn
+    hipError_t e = launch_verify(qv, st);
+    if (e == hipSuccess) e = launch_sample(qs, st);
+    return hip_status(e);
+  }
+  // verification's streaming pass; then its acceptance and residual pass
+  // beside sampling's streaming pass; then its bonus (and lookup) beside
+  // sampling's epilogue
+  Params pv = qv.p;
+  hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
+    return dispatch<LVerify>(qv.dt, qv.al, qv.g_stream, pv, st, e0, e1);
+  });
+  // fewer, longer residual workgroups: they share the GPU with the
+  // streaming pass, whose progress sets the launch's duration
+  pv.racc = CH_R * RACC_ROUND;
+  pv.nchunk = (int)cdiv(pv.NB, pv.racc);
+  const int64_t g_acc = (int64_t)pv.B * pv.nchunk;
+  if (e == hipSuccess) {
+    e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
+      return e0 ? dispatch<LRoundMidT>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st, e0, e1)
+                : dispatch<LRoundMid>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st);
+    });
+  }
+  if (e == hipSuccess) e = dispatch<LRoundTail>(qv.dt, qv.al, qv.g_tail + qs.g_tail, pv, qs.p, (int)qv.g_tail, st);
+  return hip_status(e);
+}
+
+// Scratch of ssd_round_noalloc on each GPU: the array below, whose address
+// on device d comes from hipGetSymbolAddress, taken once per device with d
+// current and kept (the array's name is a host-side stand-in, never an
+// address host code may pass on).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};
+
+ssd_status scratch_of(hipStream_t st, char** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SSD_ERR_HIP;
+  int dev = cur;
+  if (st) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(st, &d) != hipSuccess) return SSD_ERR_HIP;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return SSD_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr || (uintptr_t)ptr % 256 != 0) return SSD_ERR_HIP;
+    g_scratch[dev] = (char*)ptr;
+  }
+  *out = g_scratch[dev];
+  return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -332,6 +430,7 @@ const char* ssd_status_string(ssd_status s) {
     case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
     case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    case SSD_ERR_SCRATCH_LIMIT: return "SSD_ERR_SCRATCH_LIMIT";
   }
   return "SSD_ERR_UNKNOWN";
 }
@@ -463,56 +562,47 @@ ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
 }
 
 ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream) {
-  if (!v && !s) return SSD_ERR_INVALID_ARG;
   Plan qv, qs;
+  const ssd_status e = plan_round(v, s, qv, qs);
+  if (e != SSD_OK) return e;
+  return launch_round(v ? &qv : nullptr, s ? &qs : nullptr, (hipStream_t)stream);
+}
+
+ssd_status ssd_round_noalloc(const ssd_verify_args* v, const ssd_sample_args* s, void* stream) {
+  if (!v && !s) return SSD_ERR_INVALID_ARG;
+  // every argument is checked before any HIP call: sizes against the scratch
+  // halves, then the full plan on stand-in addresses (never dereferenced)
+  ssd_verify_args va{};
+  ssd_sample_args sa{};
   if (v) {
-    const ssd_status e = plan_verify(*v, qv);
-    if (e != SSD_OK) return e;
+    const size_t n = ssd_workspace_bytes(SSD_OP_VERIFY, v->B, v->K, v->V);
+    if (n == 0) return SSD_ERR_INVALID_ARG;
+    if (n > kScratchHalf) return SSD_ERR_SCRATCH_LIMIT;
+    va = *v;
+    va.workspace = reinterpret_cast<void*>(uintptr_t(256));
+    va.ws_bytes = kScratchHalf;
   }
   if (s) {
-    const ssd_status e = plan_sample(*s, qs);
-    if (e != SSD_OK) return e;
+    const size_t n = ssd_workspace_bytes(SSD_OP_SAMPLE, s->B, s->K, s->V);
+    if (n == 0) return SSD_ERR_INVALID_ARG;
+    if (n > kScratchHalf) return SSD_ERR_SCRATCH_LIMIT;
+    sa = *s;
+    sa.workspace = reinterpret_cast<void*>(uintptr_t(512));
+    sa.ws_bytes = kScratchHalf;
   }
-  if (v && s && (v->workspace == s->workspace)) return SSD_ERR_WORKSPACE;
-  if (v && s) {
-    // round i+1's sampling must not write what round i's verification reads
-    const void* w[] = {s->out_tokens, s->out_q, s->out_stats, s->out_topf_idx};
-    const void* r[] = {v->draft_tokens, v->draft_q, v->draft_stats, v->draft_topf_idx};
-    for (const void* a : w)
-      for (const void* b : r)
-        if (a && a == b) return SSD_ERR_INVALID_ARG;
-    if (v->cache && s->cache && v->cache->keys && v->cache->keys == s->cache->keys) return SSD_ERR_INVALID_ARG;
-  }
+  Plan qv, qs;
+  ssd_status e = plan_round(v ? &va : nullptr, s ? &sa : nullptr, qv, qs);
+  if (e != SSD_OK) return e;
   hipStream_t st = (hipStream_t)stream;
-  (void)hipGetLastError();
-  if (!v) return hip_status(launch_sample(qs, st));
-  if (!s) return hip_status(launch_verify(qv, st));
-  if (qv.dt != qs.dt || qv.al != qs.al) {
-    // kernels of different element types cannot share a launch: in turn
-    hipError_t e = launch_verify(qv, st);
-    if (e == hipSuccess) e = launch_sample(qs, st);
-    return hip_status(e);
-  }
-  // verification's streaming pass; then its acceptance and residual pass
-  // beside sampling's streaming pass; then its bonus (and lookup) beside
-  // sampling's epilogue
-  Params pv = qv.p;
-  hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
-    return dispatch<LVerify>(qv.dt, qv.al, qv.g_stream, pv, st, e0, e1);
-  });
-  // fewer, longer residual workgroups: they share the GPU with the
-  // streaming pass, whose progress sets the launch's duration
-  pv.racc = CH_R * RACC_ROUND;
-  pv.nchunk = (int)cdiv(pv.NB, pv.racc);
-  const int64_t g_acc = (int64_t)pv.B * pv.nchunk;
-  if (e == hipSuccess) {
-    e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
-      return e0 ? dispatch<LRoundMidT>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st, e0, e1)
-                : dispatch<LRoundMid>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st);
-    });
-  }
-  if (e == hipSuccess) e = dispatch<LRoundTail>(qv.dt, qv.al, qv.g_tail + qs.g_tail, pv, qs.p, (int)qv.g_tail, st);
-  return hip_status(e);
+  char* base = nullptr;
+  e = scratch_of(st, &base);
+  if (e != SSD_OK) return e;
+  // verification in the first half, sampling in the second
+  if (v) va.workspace = base;
+  if (s) sa.workspace = base + kScratchHalf;
+  e = plan_round(v ? &va : nullptr, s ? &sa : nullptr, qv, qs);
+  if (e != SSD_OK) return e;
+  return launch_round(v ? &qv : nullptr, s ? &qs : nullptr, st);
 }
 
 ssd_status ssd_cache_lookup(const int32_t* keys, const int32_t* depth_off, const int32_t* payload, int32_t B,

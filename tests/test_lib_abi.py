@@ -272,3 +272,29 @@ def test_verify_early_rejects_bad_arguments(L):
     assert f(ctypes.byref(small_ws), 2, None) == 3
     bad_c = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 1.5, 0, P, P, P, P, 2, P, P, P, None, None, ws, 1 << 24)
     assert f(ctypes.byref(bad_c), 2, None) == 1
+
+
+def test_round_noalloc_rejects_before_any_launch(L):
+    """ssd_round_noalloc refuses a request larger than its static scratch
+    (SSD_ERR_SCRATCH_LIMIT = 5) and bad arguments (SSD_ERR_INVALID_ARG),
+    all before touching the GPU; fake non-null pointers are never
+    dereferenced.  The workspace fields are ignored."""
+    import lossless_verify_sample_amd as ssd
+    P = ctypes.c_void_p(1 << 20)
+    Q = ctypes.c_void_p(1 << 26)
+    r = L.ssd_round_noalloc
+    r.argtypes = [ctypes.c_void_p] * 3
+    assert r(None, None, None) == 1
+    # B = 130, K = 7, V = 2^20: 1040 rows of 512 blocks need 8.3 MiB of partials
+    big = ssd._VerifyArgs(P, P, 1, 130, 7, 1 << 20, 1 << 20, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, None, None,
+                          None, 0)
+    assert r(ctypes.byref(big), None, None) == 5
+    bigs = ssd._SampleArgs(P, 1, 130, 7, 1 << 20, 1 << 20, P, 2, 0.5, 2, 0, Q, Q, Q, Q, Q, None, None, 0)
+    assert r(None, ctypes.byref(bigs), None) == 5
+    bad = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 1.5, 2, 0, Q, Q, Q, Q, Q, None, None, 0)
+    assert r(None, ctypes.byref(bad), None) == 1  # C > 1
+    v2 = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, Q, P, P, P, 2, P, P, P, None, None, None, 0)
+    s2 = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 0.5, 2, 0, Q, Q, Q, Q, Q, None, None, 0)
+    assert r(ctypes.byref(v2), ctypes.byref(s2), None) == 1  # sampling writes the tokens being verified
+    L.ssd_status_string.restype = ctypes.c_char_p
+    assert L.ssd_status_string(5) == b"SSD_ERR_SCRATCH_LIMIT"
