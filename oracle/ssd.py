@@ -23,6 +23,10 @@ describes in words (the target decides how many drafted tokens to accept and
 then samples one extra bonus token, and the output follows the target's
 distribution).
 
+Parity unpinned: the cost model of backoff() is a reading the pages do not
+fix (they give no formula for the back-off decision); its algebra is pinned
+(ties, the closed-form critical batch, limiting cases), its content is not.
+
 Arrays: logits z are fp64 with the vocabulary last.  A row has V entries;
 -inf marks a token of zero weight.  Temperatures that are not > 0 select the
 greedy (argmax) path.

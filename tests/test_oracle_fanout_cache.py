@@ -45,6 +45,50 @@ def _compositions(n, parts):
         yield out
 
 
+@pytest.mark.parametrize("alpha", [0.0, 0.3, 0.6, 0.95, 1.0])
+@pytest.mark.parametrize("K", [0, 1, 3, 6])
+def test_depth_probs_by_enumeration(alpha, K):
+    """P(k* = k) for K positions accepted independently with probability
+    alpha: every accept/reject pattern enumerated with its probability, k* the
+    position of the first rejection (K if none); the mean is also the closed
+    form E[k*] = alpha + alpha^2 + ... + alpha^K."""
+    want = [0.0] * (K + 1)
+    for pat in itertools.product([True, False], repeat=K):
+        pr = 1.0
+        for acc in pat:
+            pr *= alpha if acc else 1.0 - alpha
+        ks = pat.index(False) if False in pat else K
+        want[ks] += pr
+    got = O.depth_probs(alpha, K)
+    assert len(got) == K + 1
+    assert all(abs(g - w) < 1e-12 for g, w in zip(got, want))
+    assert abs(sum(got) - 1.0) < 1e-12
+    assert abs(sum(k * g for k, g in enumerate(got)) - sum(alpha ** k for k in range(1, K + 1))) < 1e-12
+
+
+def test_depth_probs_match_the_oracles_verification():
+    """depth_probs against the accepted lengths the oracle's verification
+    produces: identical target and draft rows at every position with a fixed
+    per-position acceptance rate alpha = sum_x min(p, sigma); chi-square over
+    seeds (the verification's own Philox draws)."""
+    V, K, T, F, C = 5, 3, 1.0, 1, 0.4
+    zt = np.array([0.3, -0.2, 1.1, 0.0, -1.0])
+    zd = np.array([0.9, -0.5, 0.2, 0.4, -0.3])
+    p = O.softmax_t(zt, T)["p"]
+    s = O.sigma(zd, T, F, C)["sigma"]
+    alpha = O.acceptance_rate(p, s)
+    ZT = np.tile(zt, (1, K + 1, 1))
+    ZD = np.tile(zd, (1, K + 1, 1))
+    n = 3000
+    counts = np.zeros(K + 1)
+    for seed in range(n):
+        tok = O.draft_sample(ZD, [T], F, C, seed)["tokens"]
+        counts[O.verify(ZT, ZD, [T], F, C, seed, tok)["accept_len"][0]] += 1
+    e = n * np.array(O.depth_probs(alpha, K))
+    chi2 = float(np.sum((counts - e) ** 2 / e))
+    assert chi2 < 16.27, (chi2, counts, e)  # chi-square, 3 degrees of freedom, p = 0.001
+
+
 @pytest.mark.parametrize("alpha,r", [(0.6, 1.0), (0.8, 0.5), (0.3, 2.0), (0.9, 1.5)])
 @pytest.mark.parametrize("Bgt,K", [(6, 2), (10, 3), (12, 3)])
 def test_greedy_fanout_is_optimal_by_brute_force(alpha, r, Bgt, K):
