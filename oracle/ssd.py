@@ -306,6 +306,101 @@ def verify(zt, zd, T, F, C, seed, tokens, blk=BLK, b0=0):
     return out
 
 
+# --------------------------------------------------------------------------
+# token-tree verification ([SSD-A], closing paragraph of "SSD 如何實現草擬與驗證
+# 并行？": SSD combines naturally with token-tree speculation).  The pages give
+# no algorithm; the reading is the textbook multi-candidate rule, recursive
+# rejection sampling over the drafted children of a node, with the residual
+# renormalised after each rejected sibling.  Lossless when the children of a
+# node are independent draws from the draft distribution at that node.
+# --------------------------------------------------------------------------
+def tree_children(parent):
+    """Children of every node in index order; parent[0] = -1 (the root) and
+    0 <= parent[m] < m for m >= 1."""
+    kids = [[] for _ in range(len(parent))]
+    for m in range(1, len(parent)):
+        kids[parent[m]].append(m)
+    return kids
+
+
+def tree_depth(parent):
+    d = [0] * len(parent)
+    for m in range(1, len(parent)):
+        d[m] = d[parent[m]] + 1
+    return d
+
+
+def verify_tree(zt, zd, T, F, C, seed, parent, tokens, blk=BLK, b0=0):
+    """zt, zd: [B, N+1, V] fp64, row n = node n (node 0 is the root, the last
+    accepted token's context); parent: [N+1] topology shared by the batch;
+    tokens: [B, N+1], tokens[b, m] = token of node m >= 1, drawn from sigma of
+    draft row parent[m] (entry 0 unused).
+
+    Walk from the root.  At node n with children m_1 < m_2 < ... (siblings
+    i = 0, 1, ...): r = p_n; for each sibling in turn, u = U(seed, b, j = n,
+    ACCEPT, idx = i) and accept iff u < r(x) / sigma_n(x) (+inf when sigma_n(x)
+    = 0 < r(x), 0 when both are 0 or x is outside [0, V)); on acceptance move
+    to that child; on rejection r <- max(0, r - sigma_n), renormalised (kept
+    unchanged when it has no mass).  When every sibling is rejected the bonus
+    is drawn from r; at a node without children from p_n; both with the
+    two-level sampler at (b, j = n, BONUS streams).  Greedy (T not > 0): the
+    first sibling whose token is the target row's argmax is accepted, the
+    bonus is the argmax of the node where the walk stops.
+    Returns dict(accept_len [B] (nodes accepted), last [B] (the node where the
+    walk stopped), bonus [B], acc_margin [B, N+1] (|u - ratio| of each
+    evaluated node, inf elsewhere), bonus_margin [B])."""
+    zt = np.asarray(zt, dtype=np.float64)
+    zd = np.asarray(zd, dtype=np.float64)
+    B, N1, V = zt.shape
+    kids = tree_children(parent)
+    out = dict(accept_len=np.zeros(B, np.int64), last=np.zeros(B, np.int64), bonus=np.zeros(B, np.int64),
+               acc_margin=np.full((B, N1), math.inf), bonus_margin=np.full(B, math.inf))
+    for b in range(B):
+        greedy = is_greedy(T[b])
+        n, depth = 0, 0
+        while True:
+            P = softmax_t(zt[b, n], T[b])
+            if greedy:
+                nxt = next((m for m in kids[n] if int(tokens[b, m]) == P["argmax"]), None)
+                if nxt is None:
+                    out["bonus"][b] = P["argmax"]
+                    break
+                n, depth = nxt, depth + 1
+                continue
+            if not kids[n]:
+                x, mg = gsample(P["p"], seed, b0 + b, n, ph.BONUS_TOKEN, ph.BONUS_BLOCK, blk)
+                out["bonus"][b], out["bonus_margin"][b] = x, mg
+                break
+            s = sigma(zd[b, n], T[b], F, C)["sigma"]
+            r = P["p"].copy()
+            nxt = None
+            for i, m in enumerate(kids[n]):
+                x = int(tokens[b, m])
+                if not 0 <= x < V:
+                    rho = 0.0
+                elif s[x] > 0:
+                    rho = r[x] / s[x]
+                else:
+                    rho = math.inf if r[x] > 0 else 0.0
+                u = float(ph.uniforms(seed, b0 + b, n, ph.ACCEPT, np.array([i]))[0])
+                out["acc_margin"][b, m] = abs(u - rho)
+                if u < rho:
+                    nxt = m
+                    break
+                nr = np.maximum(0.0, r - s)
+                t = np.sum(nr)
+                if t > 0:
+                    r = nr / t
+            if nxt is None:
+                x, mg = gsample(r, seed, b0 + b, n, ph.BONUS_TOKEN, ph.BONUS_BLOCK, blk)
+                out["bonus"][b], out["bonus_margin"][b] = x, mg
+                break
+            n, depth = nxt, depth + 1
+        out["accept_len"][b] = depth
+        out["last"][b] = n
+    return out
+
+
 def acceptance_rate(p, s):
     """alpha = sum_x min(p_x, s_x) ([SSD-B] core-mechanism section names the
     acceptance rate as how well the draft approximates the target; reading of
