@@ -70,6 +70,7 @@ extern "C" {
 #define SSD_MAX_V (1 << 20)    /* largest vocabulary */
 #define SSD_MAX_K 32           /* largest number of drafted tokens */
 #define SSD_MAX_F 64           /* largest top-F */
+#define SSD_MAX_TREE_NODES 64  /* largest drafted token tree, root included */
 
 typedef enum {
   SSD_OK = 0,
@@ -87,7 +88,8 @@ typedef enum {
   SSD_OP_SOFTMAX_T = 0,
   SSD_OP_TOPF = 1,
   SSD_OP_SAMPLE = 2,
-  SSD_OP_VERIFY = 3
+  SSD_OP_VERIFY = 3,
+  SSD_OP_VERIFY_TREE = 4  /* ssd_verify_tree: n = B, K = N (nodes besides the root) */
 } ssd_op;
 
 /* Per-row statistics (16 bytes).  max = largest logit; argmax = its lowest
@@ -317,6 +319,66 @@ ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* s
  * logit row and 2048 vocabulary entries), before any launch. */
 #define SSD_NOALLOC_HALF_BYTES (8u << 20)
 ssd_status ssd_round_noalloc(const ssd_verify_args* v, const ssd_sample_args* s, void* stream);
+
+/* Token-tree verification ([SSD-A], closing paragraph of "SSD 如何實現草擬與
+ * 驗證并行？": SSD combines naturally with token-tree speculation; the pages
+ * give no algorithm).  Reading: the textbook multi-candidate rule, recursive
+ * rejection sampling over each node's drafted children, lossless when the
+ * children of a node are independent draws from sigma of that node's draft
+ * row (e.g. ssd_saguaro_sample called once per child rank with its own
+ * seed).  Walking from the root: at node n with children m_1 < m_2 < ...
+ * (sibling rank i = 0, 1, ...) the residual starts as r = p_n; sibling i is
+ * accepted iff u < r(x) / sigma_n(x), u the acceptance draw at (idx = i, b,
+ * j = n); on acceptance the walk moves to it; on rejection r becomes
+ * max(0, r - sigma_n) renormalised (unchanged when it has no mass).  When
+ * every sibling is rejected the bonus is drawn from r, at a node without
+ * children from p_n, both at (b, j = n) with the bonus streams.  Greedy
+ * sequences accept the first child whose token is the target row's argmax;
+ * their bonus is the argmax where the walk stops.  A path tree (parent[m] =
+ * m - 1) gives exactly ssd_verify's accepted length and bonus.
+ * Each rejection of a sibling costs one pass over the node's target and
+ * draft rows (the residual's normaliser, needed before the next sibling).
+ *   target_logits, draft_logits  device [B, N+1, ld] rows: row n holds the
+ *                logits at node n (node 0 = the root)
+ *   parent       host int32 [N+1]: parent[0] = -1, 0 <= parent[m] < m; the
+ *                topology is shared by the batch; 0 <= N < SSD_MAX_TREE_NODES
+ *   tokens       device int32 [B, N+1]: token of node m >= 1 (entry 0
+ *                unused); ids outside [0, V) are rejected
+ *   draft_q      device float [B, N+1]: sigma_{parent[m]}(token m) (a value
+ *                <= 0 makes the ratio infinite when r > 0)
+ *   draft_stats  device ssd_row_stats [B, N+1] of the draft rows (as from
+ *                ssd_saguaro_sample with K = N); draft_topf_idx device int32
+ *                [B, N+1, ld_topf] (their first F entries are each row's S;
+ *                NULL if F = 0); temperature, F, C, seed as for ssd_verify
+ * Outputs (device int32 [B]): out_accept_len = nodes accepted (the depth of
+ *   out_last), out_last = the node where the walk stopped (its ancestors are
+ *   the accepted path), out_bonus.
+ * workspace: ssd_workspace_bytes(SSD_OP_VERIFY_TREE, B, N, V).
+ * Errors: SSD_ERR_INVALID_ARG for a NULL `a` or pointer, sizes out of range,
+ * a parent array that is not a tree in index order, bad F or C. */
+typedef struct {
+  const void* target_logits;
+  const void* draft_logits;
+  ssd_dtype dt;
+  int32_t B, N;
+  int64_t V, ld;
+  const int32_t* parent;
+  const float* temperature;
+  int32_t F;
+  float C;
+  uint64_t seed;
+  const int32_t* tokens;
+  const float* draft_q;
+  const ssd_row_stats* draft_stats;
+  const int32_t* draft_topf_idx;
+  int32_t ld_topf;
+  int32_t* out_accept_len;
+  int32_t* out_last;
+  int32_t* out_bonus;
+  void* workspace;
+  size_t ws_bytes;
+} ssd_tree_args;
+ssd_status ssd_verify_tree(const ssd_tree_args* a, void* stream);
 
 /* Speculation-cache lookup keyed by (accepted length, bonus token) ([SSD-B]
  * core-mechanism section: the draft builds a speculation cache while the

@@ -14,14 +14,15 @@ import os
 import torch  # provides the process's HIP runtime, which libssd then shares
 
 __all__ = [
-    "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "verify_early", "round_step", "cache_keys", "cache_lookup",
+    "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "verify_early", "verify_tree", "round_step",
+    "cache_keys", "cache_lookup",
     "fanout", "fanout_greedy", "backoff", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
 
 F32, BF16, F16 = 0, 1, 2
-OP_SOFTMAX_T, OP_TOPF, OP_SAMPLE, OP_VERIFY = 0, 1, 2, 3
+OP_SOFTMAX_T, OP_TOPF, OP_SAMPLE, OP_VERIFY, OP_VERIFY_TREE = 0, 1, 2, 3, 4
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 _vp, _i32, _i64, _u64, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
@@ -50,6 +51,14 @@ class _VerifyArgs(ctypes.Structure):  # ssd_verify_args
                 ("draft_tokens", _vp), ("draft_q", _vp), ("draft_stats", _vp), ("draft_topf_idx", _vp),
                 ("ld_topf", _i32), ("out_accept_len", _vp), ("out_bonus", _vp), ("out_p", _vp),
                 ("out_target_stats", _vp), ("cache", _vp), ("workspace", _vp), ("ws_bytes", _sz)]
+
+
+class _TreeArgs(ctypes.Structure):  # ssd_tree_args
+    _fields_ = [("target_logits", _vp), ("draft_logits", _vp), ("dt", ctypes.c_int), ("B", _i32), ("N", _i32),
+                ("V", _i64), ("ld", _i64), ("parent", _vp), ("temperature", _vp), ("F", _i32), ("C", _f32),
+                ("seed", _u64), ("tokens", _vp), ("draft_q", _vp), ("draft_stats", _vp), ("draft_topf_idx", _vp),
+                ("ld_topf", _i32), ("out_accept_len", _vp), ("out_last", _vp), ("out_bonus", _vp),
+                ("workspace", _vp), ("ws_bytes", _sz)]
 
 
 class _BackoffCost(ctypes.Structure):
@@ -119,6 +128,7 @@ def _load():
         "ssd_round": [_vp, _vp, _vp],
         "ssd_round_noalloc": [_vp, _vp, _vp],
         "ssd_verify_early": [_vp, _i32, _vp],
+        "ssd_verify_tree": [_vp, _vp],
         "ssd_fanout_greedy": [_vp, _vp, _i32, _i32, _i32, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
@@ -395,6 +405,47 @@ def verify_early(target, draft, temperature, F, C, seed, tokens, draft_q, draft_
     va = _VerifyArgs(*a)
     _check(_lib.ssd_verify_early(ctypes.byref(va), J, _stream(target.device)), "ssd_verify_early")
     return o
+
+
+def verify_tree(target, draft, temperature, F, C, seed, parent, tokens, draft_q, draft_stats, draft_topf_idx,
+                out=None):
+    """Token-tree verification (ssd_verify_tree) of target/draft rows [B, N+1, V]
+    (row n = node n, node 0 the root), parent: host list of N+1 ints
+    (parent[0] = -1, parent[m] < m); tokens / draft_q [B, N+1] (node m's
+    token and sigma_{parent[m]} of it; column 0 unused); draft_stats of the
+    N+1 draft rows, draft_topf_idx [B, N+1, >= F].  Returns dict(accept_len,
+    last, bonus), int32 [B] each."""
+    ld = _rows_ld(target, 3)
+    if draft.shape != target.shape or draft.dtype != target.dtype or _rows_ld(draft, 3) != ld:
+        raise SSDError("target and draft logits must share shape, dtype and row stride")
+    B, N1, V = target.shape
+    dev = target.device
+    if len(parent) != N1:
+        raise SSDError("parent must have one entry per node (N+1)")
+    _need(temperature, torch.float32, "temperature", dev)
+    if temperature.numel() != B:
+        raise SSDError("temperature must have one entry per sequence")
+    _shaped(tokens, torch.int32, (B, N1), "tokens", dev)
+    _shaped(draft_q, torch.float32, (B, N1), "draft_q", dev)
+    _stats_shaped(draft_stats, B * N1, "draft_stats", dev)
+    ldf = 0
+    if F > 0:
+        _need(draft_topf_idx, torch.int32, "draft_topf_idx", dev)
+        if draft_topf_idx.dim() != 3 or tuple(draft_topf_idx.shape[:2]) != (B, N1) or draft_topf_idx.shape[2] < F:
+            raise SSDError(f"draft_topf_idx must be [B, N+1, >= F] = [{B}, {N1}, >= {F}]")
+        ldf = draft_topf_idx.shape[-1]
+    if out is None:
+        out = {k: torch.empty(B, dtype=torch.int32, device=dev) for k in ("accept_len", "last", "bonus")}
+    for k in ("accept_len", "last", "bonus"):
+        _shaped(out[k], torch.int32, (B,), k, dev)
+    par = (ctypes.c_int32 * N1)(*[int(x) for x in parent])
+    ws = _workspace(OP_VERIFY_TREE, B, N1 - 1, V, dev)
+    a = _TreeArgs(_p(target), _p(draft), _DT[target.dtype], B, N1 - 1, V, ld, ctypes.cast(par, _vp), _p(temperature),
+                  F, float(C), int(seed) & (2 ** 64 - 1), _p(tokens), _p(draft_q), _p(draft_stats),
+                  _p(draft_topf_idx) if F > 0 else None, ldf, _p(out["accept_len"]), _p(out["last"]),
+                  _p(out["bonus"]), _p(ws), ws.numel())
+    _check(_lib.ssd_verify_tree(ctypes.byref(a), _stream(dev)), "ssd_verify_tree")
+    return out
 
 
 def round_step(verify_args=None, sample_args=None, noalloc=False):

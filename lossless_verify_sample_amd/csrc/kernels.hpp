@@ -1203,7 +1203,7 @@ __device__ __forceinline__ void stream_item(const Params& p, int item) {
   int xj = -1;  // verification: drafted token of this target row (j < K)
   if constexpr (MODE == M_VERIFY) {
     const int j = (int)(row % K1);
-    if (j < p.K) xj = p.dtok[(row / K1) * p.K + j];
+    if (j < p.K && p.dtok) xj = p.dtok[(row / K1) * p.K + j];
   }
   float v[32];
   decode_raw<DT, AL>(r0, v);
@@ -1471,6 +1471,259 @@ __global__ __launch_bounds__(EWG) void k_round_tail(Params pv, Params ps, int nv
   __shared__ ESm sm;
   if ((int)blockIdx.x < nv) residual_item<DT, AL>(pv, blockIdx.x, sm);
   else sample_epi_item<DT, AL>(ps, (int)blockIdx.x - nv, sm);
+}
+
+// ---------------------------------------------------------------------------
+// Token-tree verification: recursive rejection sampling over the drafted
+// children of each node (the residual renormalised after each rejected
+// sibling).  After m rejections at node n the residual is max(0, p - c sigma)
+// / N with scalars c and N: starting from c = 0, N = 1 (r = p), a rejection
+// sets c <- c + N and N <- sum_x max(0, p_x - c sigma_x), one pass over the
+// node's target and draft rows (kept when it has mass, as a residual without
+// mass leaves r unchanged).  One workgroup per sequence walks the tree from
+// the root; every wave takes the same decisions on its own copy of the
+// per-node values (one lane per node), and the passes split the blocks over
+// the waves.
+// ---------------------------------------------------------------------------
+constexpr int MAX_TN = 64;  // tree nodes (root included)
+
+struct TreeArgs {
+  uint64_t par[MAX_TN / 8];  // parent of node m in byte m (the root's is unused)
+  int N1;                    // nodes, root included
+  int32_t* last;             // out: node where the walk stopped [B]
+};
+
+struct TreeSm {
+  float vm[MAX_TN];
+  double vL[MAX_TN];
+  int vam[MAX_TN];
+  float R[2][MAX_NB];   // residual block sums of the current and previous pass
+  double rsum[ENW];
+};
+
+__device__ __forceinline__ int tree_parent(const TreeArgs& ta, int m) {
+  uint64_t w = ta.par[0];
+#pragma unroll
+  for (int i = 1; i < MAX_TN / 8; ++i) w = ((m >> 3) == i) ? ta.par[i] : w;
+  return (int)((w >> (8 * (m & 7))) & 0xFFu);
+}
+
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ void tree_item(const Params& p, const TreeArgs& ta, int b, ESm& sm, TreeSm& ts) {
+  const int N1 = ta.N1, NB = p.NB, V = (int)p.V, F = p.F, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const float T = p.temp[b];
+  const bool greedy = !(T > 0.f);
+  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
+  const double invT = greedy ? 0.0 : 1.0 / (double)T;
+  const int64_t r0 = (int64_t)b * N1;
+  const int64_t rs = p.ld * Dt<DT>::SZ;
+  // lane m: node m's parent, token, sigma_parent(token), the target logit at
+  // the token (row of the parent) and its own draft row statistics
+  const bool node = lane < N1;
+  const int nm = node ? lane : 0;
+  const int par = (node && lane > 0) ? tree_parent(ta, lane) : -1;
+  const int tok = (node && lane > 0) ? p.dtok[r0 + nm] : -1;
+  const float qv = (node && lane > 0) ? p.dq[r0 + nm] : 0.f;
+  const ssd_row_stats dsn = p.dstats[r0 + nm];
+  const bool tin = tok >= 0 && tok < V;
+  const float zc = tin ? load_elem<DT>(p.x + (r0 + par) * rs, tok) : 0.f;
+  // row statistics of every node from the streaming partials, two rows per
+  // wave and pass
+  for (int j0 = wave; j0 < N1; j0 += 2 * ENW) {
+    const int j1 = j0 + ENW;
+    WRow<PLN> ra, rb;
+    load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
+    load_wrow<PLN>(p.part + (r0 + min(j1, N1 - 1)) * NB, NB, rb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const WRow<PLN>& r = h ? rb : ra;
+      const int j = h ? j1 : j0;
+      if (j >= N1) break;
+      float lm = r.M[0];
+#pragma unroll
+      for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+      const float m = wave_max(lm);
+      int am = -1;
+      double wsum = 0.0;
+#pragma unroll
+      for (int i = PLN - 1; i >= 0; --i) {
+        if (!greedy) wsum += (double)block_w(r.M[i], r.S[i], m, s);
+        const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
+        if (mk) am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
+      }
+      wsum = wave_sum_d(wsum);
+      if (lane == 0) {
+        ts.vm[j] = m;
+        ts.vL[j] = greedy ? 0.0 : ln_fast(wsum);
+        ts.vam[j] = am < 0 ? 0 : am;
+      }
+    }
+  }
+  __syncthreads();
+  int n = 0, depth = 0, cur = 0;
+  double c = 0.0, Nr = 1.0;  // residual max(0, p - c sigma) / Nr at node n
+  bool res = false;          // the bonus comes from a residual with mass
+  for (;;) {
+    // the residual state belongs to the node the walk is at
+    c = 0.0;
+    Nr = 1.0;
+    res = false;
+    const uint64_t kids = __ballot(node && lane > 0 && par == n);
+    if (greedy) {
+      const uint64_t ok = __ballot(node && lane > 0 && par == n && tok == ts.vam[n]);
+      if (!ok) break;
+      n = (int)__builtin_ctzll(ok);
+      ++depth;
+      continue;
+    }
+    if (!kids) break;
+    const float mt = ts.vm[n];
+    const double Lt = ts.vL[n];
+    int next = -1;
+    uint64_t km = kids;
+    for (int i = 0; km; ++i) {
+      const int m = (int)__builtin_ctzll(km);
+      km &= km - 1ull;
+      const int x = __builtin_amdgcn_readlane(tok, m);
+      const double q = (double)rl_f(qv, m);
+      const double px = (x >= 0 && x < V) ? exp_fast(((double)rl_f(zc, m) - (double)mt) * invT - Lt) : 0.0;
+      const double num = px - c * q;
+      double rho;
+      if (!(x >= 0 && x < V)) rho = 0.0;
+      else if (q > 0.0) rho = fmax(num, 0.0) / (Nr * q);
+      else rho = px > 0.0 ? INFINITY : 0.0;
+      const double u = (double)uniform_of(draw1(p.seed, (uint32_t)i, (uint32_t)b, (uint32_t)n, ST_ACCEPT));
+      if (u < rho) {
+        next = m;
+        break;
+      }
+      // rejected: the residual with c' = c + Nr, summed per block into R[nxt]
+      const double cn = c + Nr;
+      const int nxt = cur ^ 1;
+      const float md = rl_f(dsn.max, n);
+      const double Ld = rl_d(dsn.lse, n);
+      const float ot = -mt * s, od = -md * s;
+      const double et = (double)ot + (double)mt * (double)s, ed = (double)od + (double)md * (double)s;
+      const float kf = (float)exp_fast((et - ed) * LN2 + (Lt - Ld));
+      const float nk = -(float)(cn * (double)kf), nkc = nk * p.C;
+      const int64_t row = r0 + n;
+      const unsigned char* rt = p.x + row * rs;
+      const unsigned char* rd = p.xd + row * rs;
+      const int32_t* tfrow = F > 0 ? p.dtopf + row * p.ld_dtopf : nullptr;
+      if (tid < F) sm.tf[tid] = tfrow[tid];
+      __syncthreads();
+      double wacc = 0.0;
+      for (int base = 0; base < NB; base += CH_R) {
+        const int be0 = base + wave, be1 = be0 + ENW;
+        if (be0 >= NB) break;
+        RawBlock<DT, AL> ut0, ud0, ut1, ud1;
+        if ((base + CH_R) * BLK <= V) {
+          load_raw<DT, AL, true>(rt, V, be0, lane, ut0);
+          load_raw<DT, AL, true>(rd, V, be0, lane, ud0);
+          load_raw<DT, AL, true>(rt, V, be1, lane, ut1);
+          load_raw<DT, AL, true>(rd, V, be1, lane, ud1);
+        } else {
+          load_raw<DT, AL, false>(rt, V, be0, lane, ut0);
+          load_raw<DT, AL, false>(rd, V, be0, lane, ud0);
+          load_raw<DT, AL, false>(rt, V, min(be1, NB - 1), lane, ut1);
+          load_raw<DT, AL, false>(rd, V, min(be1, NB - 1), lane, ud1);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int be = h ? be1 : be0;
+          if (be >= NB) break;
+          const RawBlock<DT, AL>& ut = h ? ut1 : ut0;
+          const RawBlock<DT, AL>& ud = h ? ud1 : ud0;
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int k = 0; k < 32; k += 2) {
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k), s, ot));
+            const float e2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k), s, od));
+            const float f1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k + 1), s, ot));
+            const float f2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k + 1), s, od));
+            a0 += fmaxf(fmaf(nk, e2, e1), 0.f);
+            a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
+          }
+          float R = wave_sum(a0 + a1);
+          // members of the draft's top-F set carry the factor C
+          for (int f = 0; f < F; ++f) {
+            const int xs = sm.tf[f];
+            if (xs >= 0 && xs < V && xs / BLK == be) {
+              constexpr int VW = Dt<DT>::VW;
+              const int off = xs - be * BLK, gi = off / VW, kk = (gi >> 6) * VW + off % VW;
+              float zt = raw_elem<DT, AL>(ut, 0), zd = raw_elem<DT, AL>(ud, 0);
+#pragma unroll
+              for (int k = 1; k < 32; ++k) {
+                zt = k == kk ? raw_elem<DT, AL>(ut, k) : zt;
+                zd = k == kk ? raw_elem<DT, AL>(ud, k) : zd;
+              }
+              zt = rl_f(zt, gi & 63);
+              zd = rl_f(zd, gi & 63);
+              const float e1 = __builtin_amdgcn_exp2f(fmaf(zt, s, ot));
+              const float e2 = __builtin_amdgcn_exp2f(fmaf(zd, s, od));
+              R += fmaxf(fmaf(nkc, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
+            }
+          }
+          R = fmaxf(R, 0.f);
+          if (lane == 0) ts.R[nxt][be] = R;
+          wacc += (double)R;
+        }
+      }
+      if (lane == 0) ts.rsum[wave] = wacc;
+      __syncthreads();
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < ENW; ++w) tot += ts.rsum[w];
+      // back to probability units: p_x = e1 2^(-et) e^(-Lt)
+      const double Nn = tot * exp_fast(-et * LN2 - Lt);
+      if (Nn > 0.0) {
+        c = cn;
+        Nr = Nn;
+        cur = nxt;
+        res = true;
+      }
+      __syncthreads();  // (the next pass rewrites the other buffer and the top-F list)
+    }
+    if (next < 0) break;
+    n = next;
+    ++depth;
+  }
+  if (tid == 0) {
+    p.acc_len[b] = depth;
+    ta.last[b] = n;
+    if (greedy) p.bonus[b] = ts.vam[n];
+  }
+  if (greedy) return;
+  // bonus at node n: from the residual of the last pass with mass, else
+  // from p_n (a leaf, or no rejection left any residual mass)
+  SeqState ss{};
+  ss.kstar = n;
+  ss.s = s;
+  ss.m_t = ts.vm[n];
+  ss.invT = invT;
+  const float md = rl_f(dsn.max, n);
+  const double Ld = rl_d(dsn.lse, n);
+  ss.D0 = ((double)ss.m_t - (double)md) * invT + ts.vL[n] - Ld + (res ? ln_fast(c) : 0.0);
+  ss.lnC = ln_fast((double)p.C);
+  float R[NBT], Mt[NBT];
+  const float4* tp = p.part + (r0 + n) * NB;
+#pragma unroll
+  for (int k = 0; k < NBT; ++k) {
+    const int be = tid + k * EWG;
+    const bool in = be < NB;
+    Mt[k] = in ? tp[min(be, NB - 1)].x : -INFINITY;
+    R[k] = (in && res) ? ts.R[cur][be] : 0.f;
+  }
+  epi_residual<DT, AL>(p, b, ss, R, Mt, false, sm);
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(EWG) void k_tree(Params p, TreeArgs ta) {
+  __shared__ ESm sm;
+  __shared__ TreeSm ts;
+  if (p.NB <= 128) tree_item<DT, AL, 2>(p, ta, blockIdx.x, sm, ts);
+  else tree_item<DT, AL, NBL>(p, ta, blockIdx.x, sm, ts);
 }
 
 // Dense probabilities for ssd_softmax_t (after the statistics kernel).

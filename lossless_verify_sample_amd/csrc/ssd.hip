@@ -41,9 +41,12 @@ struct Layout {
 bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   if (n < 1 || V < 1 || V > SSD_MAX_V) return false;
   if ((op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY) && (K < 0 || K > SSD_MAX_K)) return false;
-  if (op != SSD_OP_SOFTMAX_T && op != SSD_OP_TOPF && op != SSD_OP_SAMPLE && op != SSD_OP_VERIFY) return false;
+  if (op == SSD_OP_VERIFY_TREE && (K < 0 || K >= SSD_MAX_TREE_NODES)) return false;
+  if (op != SSD_OP_SOFTMAX_T && op != SSD_OP_TOPF && op != SSD_OP_SAMPLE && op != SSD_OP_VERIFY &&
+      op != SSD_OP_VERIFY_TREE)
+    return false;
   const int64_t NB = nblocks(V);
-  const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY) ? n * (K + 1) : n;
+  const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY || op == SSD_OP_VERIFY_TREE) ? n * (K + 1) : n;
   L->part = 0;
   L->state = L->rpart = L->zcap = 0;
   size_t end = al256((size_t)(rows * NB) * sizeof(float4));
@@ -98,6 +101,14 @@ SSD_LAUNCHER_E(LSampleEpi, (k_epi<DT, AL, M_SAMPLE>))
 SSD_LAUNCHER_E(LAccept, (k_accept<DT, AL>))
 SSD_LAUNCHER_E(LResidualEpi, (k_residual_epi<DT, AL>))
 SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
+
+template <int DT, bool AL>
+struct LTree {
+  static hipError_t go(int64_t grid, const Params& p, const TreeArgs& ta, hipStream_t st) {
+    k_tree<DT, AL><<<dim3((unsigned)grid), dim3(EWG), 0, st>>>(p, ta);
+    return hipGetLastError();
+  }
+};
 
 // A launch of two parameter sets (verification's kernel beside sampling's).
 #define SSD_LAUNCHER2(NAME, KERNEL)                                                          \
@@ -388,6 +399,56 @@ ssd_status launch_round(const Plan* pqv, const Plan* pqs, hipStream_t st) {
   return hip_status(e);
 }
 
+// Token-tree verification: checks, kernel parameters and the topology.
+ssd_status plan_tree(const ssd_tree_args& a, Plan& q, TreeArgs& ta) {
+  const int32_t B = a.B, N = a.N, F = a.F;
+  const int64_t V = a.V, ld = a.ld;
+  const float C = a.C;
+  if (!a.target_logits || !a.draft_logits || !a.temperature || !a.parent || !dt_ok(a.dt)) return SSD_ERR_INVALID_ARG;
+  if (!a.draft_stats || !a.out_accept_len || !a.out_last || !a.out_bonus) return SSD_ERR_INVALID_ARG;
+  if (B < 1 || N < 0 || N >= SSD_MAX_TREE_NODES || V < 1 || V > SSD_MAX_V || ld < V) return SSD_ERR_INVALID_ARG;
+  if (N > 0 && (!a.tokens || !a.draft_q)) return SSD_ERR_INVALID_ARG;
+  if (F < 0 || F > SSD_MAX_F || F > V) return SSD_ERR_INVALID_ARG;
+  if (F > 0 && (!a.draft_topf_idx || a.ld_topf < F)) return SSD_ERR_INVALID_ARG;
+  if (!(C > 0.f) || !(C <= 1.f)) return SSD_ERR_INVALID_ARG;
+  if (a.parent[0] != -1) return SSD_ERR_INVALID_ARG;
+  ta = TreeArgs{};
+  for (int m = 1; m <= N; ++m) {
+    const int pm = a.parent[m];
+    if (pm < 0 || pm >= m) return SSD_ERR_INVALID_ARG;
+    ta.par[m >> 3] |= (uint64_t)(uint8_t)pm << (8 * (m & 7));
+  }
+  ta.N1 = N + 1;
+  ta.last = a.out_last;
+  Layout L;
+  if (!layout(SSD_OP_VERIFY_TREE, B, N, V, &L)) return SSD_ERR_INVALID_ARG;
+  if (!ws_ok(a.workspace, a.ws_bytes, L)) return SSD_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * (N + 1);
+  const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
+  if (rows * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  Params& p = q.p;
+  p = Params{};
+  p.x = (const unsigned char*)a.target_logits;
+  p.xd = (const unsigned char*)a.draft_logits;
+  p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
+  p.K = N; p.B = B;
+  p.temp = a.temperature;
+  p.F = F; p.C = C; p.seed = a.seed;
+  p.part = (float4*)((char*)a.workspace + L.part);
+  p.dtok = a.tokens;
+  p.dq = a.draft_q;
+  p.dstats = a.draft_stats;
+  p.dtopf = F > 0 ? a.draft_topf_idx : nullptr;
+  p.ld_dtopf = a.ld_topf;
+  p.acc_len = a.out_accept_len;
+  p.bonus = a.out_bonus;
+  q.dt = a.dt;
+  q.al = aligned16(a.target_logits, ld, V, a.dt) && aligned16(a.draft_logits, ld, V, a.dt);
+  q.g_stream = rows * nch;
+  q.g_tail = B;
+  return SSD_OK;
+}
+
 // Scratch of ssd_round_noalloc on each GPU: the array below, whose address
 // on device d comes from hipGetSymbolAddress, taken once per device with d
 // current and kept (the array's name is a host-side stand-in, never an
@@ -603,6 +664,23 @@ ssd_status ssd_round_noalloc(const ssd_verify_args* v, const ssd_sample_args* s,
   e = plan_round(v ? &va : nullptr, s ? &sa : nullptr, qv, qs);
   if (e != SSD_OK) return e;
   return launch_round(v ? &qv : nullptr, s ? &qs : nullptr, st);
+}
+
+ssd_status ssd_verify_tree(const ssd_tree_args* a, void* stream) {
+  if (!a) return SSD_ERR_INVALID_ARG;
+  Plan q;
+  TreeArgs ta;
+  const ssd_status e0 = plan_tree(*a, q, ta);
+  if (e0 != SSD_OK) return e0;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  // every node's target row streamed once (no drafted-token capture: a
+  // node's children are evaluated at its row), then the walk
+  Params ps = q.p;
+  ps.dtok = nullptr;
+  hipError_t e = dispatch<LVerify>(q.dt, q.al, q.g_stream, ps, st);
+  if (e == hipSuccess) e = dispatch<LTree>(q.dt, q.al, q.g_tail, q.p, ta, st);
+  return hip_status(e);
 }
 
 ssd_status ssd_cache_lookup(const int32_t* keys, const int32_t* depth_off, const int32_t* payload, int32_t B,

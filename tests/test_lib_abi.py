@@ -298,3 +298,31 @@ def test_round_noalloc_rejects_before_any_launch(L):
     assert r(ctypes.byref(v2), ctypes.byref(s2), None) == 1  # sampling writes the tokens being verified
     L.ssd_status_string.restype = ctypes.c_char_p
     assert L.ssd_status_string(5) == b"SSD_ERR_SCRATCH_LIMIT"
+
+
+def test_verify_tree_rejects_bad_arguments(L):
+    """ssd_verify_tree checks the topology, sizes, F, C and the workspace
+    before any launch (fake non-null pointers are never dereferenced)."""
+    import lossless_verify_sample_amd as ssd
+    P = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 24)
+    f = L.ssd_verify_tree
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, None) == 1
+
+    def args(parent, N=None, F=2, C=0.5, wsb=1 << 24, tokens=P):
+        par = (ctypes.c_int32 * len(parent))(*parent)
+        a = ssd._TreeArgs(P, P, 1, 2, len(parent) - 1 if N is None else N, 100, 100, ctypes.cast(par, ctypes.c_void_p),
+                          P, F, C, 0, tokens, P, P, P, 2, P, P, P, ws, wsb)
+        a._keep = par
+        return a
+    ok = [-1, 0, 0, 1]
+    for bad in ([0, 0, 0, 1], [-1, 1, 0, 1], [-1, 0, 3, 1], [-1, -1, 0, 1]):
+        assert f(ctypes.byref(args(bad)), None) == 1, bad
+    assert f(ctypes.byref(args(ok, C=1.5)), None) == 1
+    assert f(ctypes.byref(args(ok, F=65)), None) == 1
+    assert f(ctypes.byref(args(ok, tokens=None)), None) == 1
+    assert f(ctypes.byref(args([-1] + [0] * 64)), None) == 1  # 65 nodes
+    assert f(ctypes.byref(args(ok, wsb=64)), None) == 3
+    assert ssd.workspace_bytes(ssd.OP_VERIFY_TREE, 2, 3, 100) > 0
+    assert ssd.workspace_bytes(ssd.OP_VERIFY_TREE, 2, 64, 100) == 0
