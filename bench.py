@@ -16,6 +16,7 @@ Infinity Cache cannot serve them.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config N] [--no-cache] [--no-cpu-baseline]
   python bench.py --copy-gib G   (plain device copy of G GiB, for counter calibration)
+  python bench.py --read-gib G   (the library's streaming-read probe over G GiB: the read ceiling)
 
 Roofline: the dominant kernel of the headline schedule, the longer of its two
 HBM-bound launches: the shared launch k_round_mid (sampling's streaming pass
@@ -63,6 +64,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-input-gib", type=float, default=1.1)
     ap.add_argument("--copy-gib", type=float, default=0.0)
+    ap.add_argument("--read-gib", type=float, default=0.0)
+    ap.add_argument("--read-variants", default="all")
+    ap.add_argument("--read-chunk-mb", type=float, default=0.0)
     return ap.parse_args()
 
 
@@ -113,6 +117,45 @@ def copy_calibration(gib):
                       "gbs": round(2 * n * 4 / el / 1e9, 1)}), flush=True)
 
 
+def read_ceiling(gib, variants, chunk_mb):
+    """The library's streaming-read probe (ssd_read_probe) over a buffer of
+    `gib` GiB, larger than the 256 MB Infinity Cache: each launch layout read
+    3 times untimed, then 10 times timed with HIP events on the probe's
+    stream.  With chunk_mb > 0 every launch reads one chunk of that many MB
+    (10^6 bytes), the chunks taken in turn, so launches of a streaming pass's
+    size are timed with their ramp-up and drain.  Prints one JSON line per
+    layout and one with the best."""
+    import torch
+
+    import lossless_verify_sample_amd as ssd
+    n = int(gib * 2 ** 30) // 16 * 16
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    cw = int(chunk_mb * 1e6) // 16 * 4 if chunk_mb > 0 else n // 4  # int32 words per launch
+    chunks = [buf[i:i + cw] for i in range(0, n // 4 - cw + 1, cw)]
+    out = None
+    best = None
+    for v in (range(12) if variants == "all" else [int(x) for x in variants.split(",")]):
+        for i in range(3):
+            out = ssd.read_probe(chunks[i % len(chunks)], v, out)
+        torch.cuda.synchronize()
+        reps = max(10, 2 * len(chunks))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            ssd.read_probe(chunks[i % len(chunks)], v, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nb = cw * 4
+        gbs = nb / (ms * 1e-3) / 1e9
+        line = {"read_probe_variant": v, "bytes_per_launch": nb, "launches": reps, "buffer_bytes": n,
+                "ms": round(ms, 5), "gbs": round(gbs, 1), "frac_of_8000": round(gbs / HBM_PEAK_GBS, 4)}
+        print(json.dumps(line), flush=True)
+        if best is None or gbs > best["gbs"]:
+            best = line
+    print(json.dumps({"read_ceiling": best}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -121,6 +164,9 @@ def main():
         sys.exit(2)
     if a.copy_gib > 0:
         copy_calibration(a.copy_gib)
+        return
+    if a.read_gib > 0:
+        read_ceiling(a.read_gib, a.read_variants, a.read_chunk_mb)
         return
     import torch
 

@@ -476,6 +476,26 @@ size_t ssd_workspace_bytes(ssd_op op, int64_t n, int32_t K, int64_t V);
 /* Static string naming a status. */
 const char* ssd_status_string(ssd_status s);
 
+/* Streaming-read probe, a measurement aid (not part of the method): reads
+ * `bytes` of device memory at `buf` (16-byte aligned) once with 16-byte loads
+ * and folds them into one word per workgroup, in one of several launch
+ * layouts, so that the read bandwidth the streaming passes can reach is
+ * measured by this library on the same part.  variant: 0 one-shot grid of
+ * 256-thread workgroups with 8 loads per thread in flight, nontemporal (the
+ * streaming passes' layout); 1 the same with 16 loads; 2, 3 with 512 and
+ * 1024 threads; 4 as 0 with ordinary loads; 5, 6 persistent grids of 8 x 256
+ * and 4 x 512 threads per compute unit, the next chunk's loads issued before
+ * the current one is folded; 7, 8 4 loads per thread with 256 and 1024
+ * threads; 9 persistent, 2 x 1024 threads per compute unit, 4 loads; 10 as 0
+ * with consecutive chunks kept on one XCD; 11 512 threads with 16 loads.
+ *   out  device uint32 [out_len], out_len >= the grid (bytes / 16 / (threads
+ *        x loads) workgroups for the one-shot variants); its contents are
+ *        not meaningful.
+ * Errors: SSD_ERR_INVALID_ARG for a bad pointer, size or variant;
+ * SSD_ERR_UNSUPPORTED when out_len is too small. */
+ssd_status ssd_read_probe(const void* buf, size_t bytes, int32_t variant, uint32_t* out, size_t out_len,
+                          void* stream);
+
 /* Kernel timer, a measurement aid (not part of the method).  While enabled,
  * every launch of the streaming pass -- the kernel that reads each logit row
  * once from HBM, in ssd_softmax_t, ssd_topf, ssd_saguaro_sample and

@@ -132,6 +132,7 @@ def _load():
         "ssd_fanout_greedy": [_vp, _vp, _i32, _i32, _i32, _vp],
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
+        "ssd_read_probe": [_vp, _sz, _i32, _vp, _sz, _vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -217,6 +218,19 @@ def _rows_ld(x, nd):
     if nd == 3 and x.stride(0) != x.shape[1] * ld:
         raise SSDError("logits rows must be evenly spaced")
     return ld
+
+
+def read_probe(buf, variant=0, out=None):
+    """Streaming-read probe (ssd_read_probe): one read of the device tensor
+    `buf` in launch layout `variant`; returns the scratch output tensor."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise SSDError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(nbytes // 16 // 512 + 1024, dtype=torch.int32, device=buf.device)
+    _check(_lib.ssd_read_probe(_p(buf), nbytes, int(variant), _p(out), out.numel(), _stream(buf.device)),
+           "ssd_read_probe")
+    return out
 
 
 def timer_enable(max_launches):

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -12,6 +13,7 @@
 #include <hip/hip_ext.h>
 
 #include "kernels.hpp"
+#include "probe.hpp"
 
 using namespace ssd;
 
@@ -710,6 +712,51 @@ ssd_status ssd_cache_keys(const int32_t* topf_idx, int32_t ld_topf, const int32_
   (void)hipGetLastError();
   k_cache_keys<<<dim3((unsigned)cdiv(n, WG)), dim3(WG), 0, (hipStream_t)stream>>>(topf_idx, ld_topf, depth_off,
                                                                                   B, K, Bgt, out_keys);
+  return hip_status(hipGetLastError());
+}
+
+ssd_status ssd_read_probe(const void* buf, size_t bytes, int32_t variant, uint32_t* out, size_t out_len,
+                          void* stream) {
+  if (!buf || !out || bytes < 16 || (uintptr_t)buf % 16 != 0) return SSD_ERR_INVALID_ARG;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipStream_t st = (hipStream_t)stream;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return SSD_ERR_HIP;
+  // (threads, loads per thread, nontemporal, grid kind, workgroups per CU)
+  struct V { int wgt, l; bool nt; int kind; int per_cu; };
+  static const V vs[] = {
+      {256, 8, true, 0, 0},  {256, 16, true, 0, 0}, {512, 8, true, 0, 0},  {1024, 8, true, 0, 0},
+      {256, 8, false, 0, 0}, {256, 8, true, 2, 8},  {512, 8, true, 2, 4},  {256, 4, true, 0, 0},
+      {1024, 4, true, 0, 0}, {1024, 4, true, 2, 2}, {256, 8, true, 1, 0},  {512, 16, true, 0, 0},
+  };
+  if (variant < 0 || variant >= (int)(sizeof(vs) / sizeof(vs[0]))) return SSD_ERR_INVALID_ARG;
+  const V v = vs[variant];
+  const int64_t nchunk = cdiv(n16, (int64_t)v.wgt * v.l);
+  const int64_t grid = v.kind == 2 ? std::min<int64_t>(nchunk, (int64_t)ncu * v.per_cu) : nchunk;
+  if (grid > kMaxGrid || (size_t)grid > out_len) return SSD_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const u32x4* p = (const u32x4*)buf;
+  const dim3 g((unsigned)grid);
+#define SSD_PROBE_ONCE(W, LL, N, X) k_probe_once<W, LL, N, X><<<g, dim3(W), 0, st>>>(p, n16, out)
+#define SSD_PROBE_PERSIST(W, LL, N) k_probe_persist<W, LL, N><<<g, dim3(W), 0, st>>>(p, n16, nchunk, out)
+  switch (variant) {
+    case 0: SSD_PROBE_ONCE(256, 8, true, false); break;
+    case 1: SSD_PROBE_ONCE(256, 16, true, false); break;
+    case 2: SSD_PROBE_ONCE(512, 8, true, false); break;
+    case 3: SSD_PROBE_ONCE(1024, 8, true, false); break;
+    case 4: SSD_PROBE_ONCE(256, 8, false, false); break;
+    case 5: SSD_PROBE_PERSIST(256, 8, true); break;
+    case 6: SSD_PROBE_PERSIST(512, 8, true); break;
+    case 7: SSD_PROBE_ONCE(256, 4, true, false); break;
+    case 8: SSD_PROBE_ONCE(1024, 4, true, false); break;
+    case 9: SSD_PROBE_PERSIST(1024, 4, true); break;
+    case 10: SSD_PROBE_ONCE(256, 8, true, true); break;
+    case 11: SSD_PROBE_ONCE(512, 16, true, false); break;
+  }
+#undef SSD_PROBE_ONCE
+#undef SSD_PROBE_PERSIST
   return hip_status(hipGetLastError());
 }
 
