@@ -17,6 +17,7 @@ Infinity Cache cannot serve them.  Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--config N] [--no-cache] [--no-cpu-baseline]
   python bench.py --copy-gib G   (plain device copy of G GiB, for counter calibration)
   python bench.py --read-gib G   (the library's streaming-read probe over G GiB: the read ceiling)
+  python bench.py --phases       (phase timings of the epilogues; needs the instrumented libssd_phases.so)
 
 Roofline: the dominant kernel of the headline schedule, the longer of its two
 HBM-bound launches: the shared launch k_round_mid (sampling's streaming pass
@@ -67,6 +68,7 @@ def parse():
     ap.add_argument("--read-gib", type=float, default=0.0)
     ap.add_argument("--read-variants", default="all")
     ap.add_argument("--read-chunk-mb", type=float, default=0.0)
+    ap.add_argument("--phases", action="store_true")
     return ap.parse_args()
 
 
@@ -156,6 +158,61 @@ def read_ceiling(gib, variants, chunk_mb):
     print(json.dumps({"read_ceiling": best}), flush=True)
 
 
+def phases(a):
+    """Phase timings of the latency-bound kernels from the instrumented
+    library (libssd_phases.so, built by `python -m
+    lossless_verify_sample_amd.build --phases`): the workload's sampling and
+    verification as separate calls, with the cache step, a few times; then
+    per phase the median, 90th percentile and maximum over the items of the
+    last call (rows for the sampling epilogue, sequences for acceptance and
+    bonus), in microseconds, and the spread from the first item's start to
+    the last item's end.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import lossless_verify_sample_amd as ssd
+    from lossless_verify_sample_amd import workloads as W
+    ssd.use_library(os.path.join(ROOT, "lossless_verify_sample_amd", "libssd_phases.so"))
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[a.config]
+    B, K, V = cfg.B, cfg.K, cfg.V
+    T = W.temperatures(cfg, dev)
+    Fk = ssd.fanout(a.cache_budget, K, a.cache_ratio, V)
+    for it in range(4):
+        t, d = W.logits(cfg, it, dev)
+        cache = ssd.Cache(Fk, B, K, dev, payload=W.payload(cfg, a.cache_budget, it, dev), miss_fill=True)
+        s = ssd.saguaro_sample(d, T, cfg.F, cfg.C, W.seed(cfg, it), F_out=cfg.fout, cache=cache)
+        v = ssd.verify(t, d, T, cfg.F, cfg.C, W.seed(cfg, it), s["tokens"], s["q"], s["stats"], s["topf_idx"],
+                       cache=cache)
+    torch.cuda.synchronize()
+    acc = v["accept_len"].cpu().numpy()
+    names = {0: ["partials loaded, row maximum", "block weights summed", "top-F list",
+                 "sigma normaliser and outputs", "block drawn", "chosen block re-read, token drawn"],
+             1: ["K+1 rows' statistics", "acceptance decisions", "residual sums of the chunk"],
+             2: ["residual sums in hand", "block drawn", "chosen block re-read", "token drawn", "cache lookup"]}
+    items = {0: B * (K + 1), 1: B, 2: B}
+    Tb = T.cpu().numpy()
+    keep = {0: (np.arange(B * (K + 1)) % (K + 1) < K) & (np.repeat(Tb, K + 1) > 0),  # sampled rows
+            1: (acc < K) & (Tb > 0),                                  # sequences with a residual
+            2: (acc < K) & (Tb > 0)}
+    out = {"metric": "phase timings of the latency-bound kernels", "unit": "us", "config": cfg.name,
+           "B": B, "K": K, "V": V, "cache_fanout": Fk}
+    for kind in (0, 1, 2):
+        st = ssd.phase_read(kind, items[kind])[keep[kind]]
+        n = len(names[kind])
+        ph = {}
+        for k in range(n):
+            dd = (st[:, k + 1] - st[:, k]) * 0.01
+            ph[names[kind][k]] = {"median": round(float(np.median(dd)), 3), "p90": round(float(np.percentile(dd, 90)), 3),
+                                  "max": round(float(dd.max()), 3)}
+        tot = (st[:, n] - st[:, 0]) * 0.01
+        out[["sampling_epilogue", "acceptance_pass", "bonus"][kind]] = {
+            "items": int(len(st)), "phases": ph,
+            "item_total": {"median": round(float(np.median(tot)), 3), "max": round(float(tot.max()), 3)},
+            "first_start_to_last_end": round(float((st[:, n].max() - st[:, 0].min()) * 0.01), 3)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -167,6 +224,9 @@ def main():
         return
     if a.read_gib > 0:
         read_ceiling(a.read_gib, a.read_variants, a.read_chunk_mb)
+        return
+    if a.phases:
+        phases(a)
         return
     import torch
 

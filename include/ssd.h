@@ -496,6 +496,24 @@ const char* ssd_status_string(ssd_status s);
 ssd_status ssd_read_probe(const void* buf, size_t bytes, int32_t variant, uint32_t* out, size_t out_len,
                           void* stream);
 
+/* Phase stamps, a measurement aid of the instrumented build only (compiled
+ * with -DSSD_PHASES; `python -m lossless_verify_sample_amd.build --phases`
+ * writes libssd_phases.so): the latency-bound kernels record the 100 MHz
+ * real-time counter (10 ns per tick) at fixed points, 8 slots per item:
+ *   kind 0: sampling epilogue, item = row b*(K+1)+j: start, partials loaded,
+ *           block weights summed, top-F list, sigma normaliser and outputs,
+ *           block drawn, token drawn;
+ *   kind 1: acceptance and residual pass, item = sequence (its first chunk's
+ *           workgroup): start, statistics of the K+1 rows, decisions, the
+ *           chunk's residual sums;
+ *   kind 2: bonus and lookup, item = sequence: start, residual sums in hand,
+ *           block drawn, chosen block re-read, token drawn, lookup done.
+ * ssd_phase_read copies the first n stamps of `kind` (item * 8 + slot, up to
+ * 8192 items; slots an item does not reach keep older values) to host `out`.
+ * Errors: SSD_ERR_UNSUPPORTED in the ordinary build; SSD_ERR_INVALID_ARG for
+ * a bad kind, pointer or count. */
+ssd_status ssd_phase_read(int32_t kind, uint64_t* out, int64_t n);
+
 /* Kernel timer, a measurement aid (not part of the method).  While enabled,
  * every launch of the streaming pass -- the kernel that reads each logit row
  * once from HBM, in ssd_softmax_t, ssd_topf, ssd_saguaro_sample and

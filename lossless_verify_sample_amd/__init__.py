@@ -17,6 +17,7 @@ __all__ = [
     "SSDError", "Cache", "softmax_t", "topf", "saguaro_sample", "verify", "verify_early", "verify_tree", "round_step",
     "cache_keys", "cache_lookup",
     "fanout", "fanout_greedy", "backoff", "workspace_bytes", "stats_fields", "timer_enable", "timer_read", "LIB_PATH",
+    "use_library", "phase_read", "read_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
@@ -133,6 +134,7 @@ def _load():
         "ssd_cache_keys": [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp],
         "ssd_fanout": [_i32, _i32, _f64, _i64, _vp],
         "ssd_read_probe": [_vp, _sz, _i32, _vp, _sz, _vp],
+        "ssd_phase_read": [_i32, _vp, _i64],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -147,6 +149,15 @@ def _load():
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     return lib
+
+
+def use_library(path):
+    """Load libssd from `path` instead of the package's libssd.so (e.g. the
+    instrumented libssd_phases.so); only before the library is first used."""
+    global LIB_PATH
+    if _Lazy.lib is not None:
+        raise SSDError("the library is already loaded")
+    LIB_PATH = path
 
 
 class _Lazy:
@@ -231,6 +242,15 @@ def read_probe(buf, variant=0, out=None):
     _check(_lib.ssd_read_probe(_p(buf), nbytes, int(variant), _p(out), out.numel(), _stream(buf.device)),
            "ssd_read_probe")
     return out
+
+
+def phase_read(kind, items):
+    """Phase stamps of the instrumented build (ssd_phase_read): int64 numpy
+    array [items, 8] of 100 MHz ticks."""
+    import numpy as np
+    out = np.zeros(items * 8, dtype=np.uint64)
+    _check(_lib.ssd_phase_read(int(kind), out.ctypes.data_as(_vp), items * 8), "ssd_phase_read")
+    return out.astype(np.int64).reshape(items, 8)
 
 
 def timer_enable(max_launches):

@@ -1,6 +1,9 @@
 """Build libssd.so (HIP, gfx950) in-tree with hipcc.
 
-python -m lossless_verify_sample_amd.build
+python -m lossless_verify_sample_amd.build [--phases]
+
+--phases builds the instrumented libssd_phases.so instead (phase stamps of
+the latency-bound kernels, read with ssd_phase_read; a measurement aid).
 """
 import os
 import shutil
@@ -11,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ssd.hip")
 OUT = os.path.join(HERE, "libssd.so")
+OUT_PHASES = os.path.join(HERE, "libssd_phases.so")
 ARCH = os.environ.get("SSD_OFFLOAD_ARCH", "gfx950")
 
 
@@ -21,9 +25,10 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def command(out):
+def command(out, phases=False):
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        *(["-DSSD_PHASES"] if phases else []),
         # no FMA contraction: the host fan-out and the device offset bookkeeping
         # rely on plain IEEE operations; fused multiply-adds are written out
         "-ffp-contract=off",
@@ -34,9 +39,10 @@ def command(out):
     ]
 
 
-def build(verbose=True):
-    tmp = OUT + ".tmp"
-    cmd = command(tmp)
+def build(verbose=True, phases=False):
+    out = OUT_PHASES if phases else OUT
+    tmp = out + ".tmp"
+    cmd = command(tmp, phases)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,10 +51,10 @@ def build(verbose=True):
         raise RuntimeError("hipcc failed:\n" + msg)
     if verbose and msg.strip():
         print(msg)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(phases="--phases" in sys.argv[1:])
     sys.exit(0)

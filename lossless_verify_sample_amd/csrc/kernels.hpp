@@ -23,6 +23,27 @@
 
 namespace ssd {
 
+// Phase stamps of the latency-bound kernels, compiled in only for the
+// instrumented build (-DSSD_PHASES, a measurement aid): the first lane of
+// wave 0 records the 100 MHz real-time counter at fixed points of each item
+// (kind 0: sampling epilogue, per row; kind 1: acceptance and residual pass,
+// the first chunk of each sequence; kind 2: bonus and cache lookup, per
+// sequence).
+constexpr int PH_N = 8;
+constexpr int PH_ITEMS = 8192;
+#ifdef SSD_PHASES
+__device__ uint64_t g_phase[3][PH_ITEMS * PH_N];
+#define SSD_PHASE(kind, item, k)                                                              \
+  do {                                                                                        \
+    if (threadIdx.x == 0 && (int64_t)(item) < PH_ITEMS)                                       \
+      g_phase[kind][(int64_t)(item) * PH_N + (k)] = __builtin_amdgcn_s_memrealtime();          \
+  } while (0)
+#else
+#define SSD_PHASE(kind, item, k) \
+  do {                           \
+  } while (0)
+#endif
+
 enum Mode { M_SOFTMAX = 0, M_TOPF = 1, M_SAMPLE = 2, M_VERIFY = 3 };
 
 constexpr int CH = 8;             // blocks per workgroup in the streaming pass (2 per wave)
@@ -716,6 +737,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   const int NB = p.NB, V = (int)p.V, F = p.F;
   const float C = p.C;
   const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
+  SSD_PHASE(0, row, 0);
   if (tid == 0) sm.nre = 0;
   const bool draw = !greedy && j < p.K;
   WRow<PLN> r;
@@ -731,6 +753,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
 #pragma unroll
   for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
   const float m = wave_max(lm);
+  SSD_PHASE(0, row, 1);  // partials loaded, row maximum
   float w[PLN];
   double ws = 0.0;
 #pragma unroll
@@ -739,10 +762,12 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
     ws += (double)w[i];
   }
   const double tot0 = greedy ? 1.0 : wave_sum_d(ws);
+  SSD_PHASE(0, row, 2);  // block weights and their sum
   // entries ranked: F for sigma and F_out listed; this depth's cache keys
   // when they fit in that list (longer key lists have workgroups of their own)
   const int Fj = p.ckeys ? p.koff[j + 1] - p.koff[j] : 0;
   const uint64_t tkey = wave_topf<DT, AL, PLN>(rp, V, NB, p.F_sel, r, m, sm);
+  SSD_PHASE(0, row, 3);  // top-F list
   const float tv = key_val(tkey);
   const int ti = (int)key_idx(tkey);
   // sigma_{F,C}: lane f < F holds 2^((z_f - m) s) of the f-th member of S
@@ -763,6 +788,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
       p.stats[row] = st;
     }
   }
+  SSD_PHASE(0, row, 4);  // sigma normaliser, statistics and lists written
   if (j == p.K) return;  // row K only predicts the bonus after K acceptances
   if (greedy) {
     if (tid == 0) {
@@ -790,6 +816,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   }
   bk = wave_min_u64(bk);
   const int beta = bk == NO_KEY ? 0 : (int)(uint32_t)bk;  // no block of mass only for invalid rows
+  SSD_PHASE(0, row, 5);  // block drawn
   // token stage over block beta
   const int x0 = beta * BLK + TPT * tid;
   Run<DT, AL> run;
@@ -805,6 +832,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
     if (!(z[e] > -INFINITY)) return INFINITY;
     return (Mb - z[e]) * s + (((smask >> e) & 1u) ? nc2 : 0.f);
   });
+  SSD_PHASE(0, row, 6);  // chosen block re-read and token race
   const uint32_t d = (uint32_t)(x - x0);
   if (x >= 0 && d < (uint32_t)TPT) {
     // the owner of the winning token writes it with sigma_j(x)
@@ -865,6 +893,7 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
   const int64_t r0 = (int64_t)b * K1;
   const int64_t rs = p.ld * Dt<DT>::SZ;
   const bool lead = chunk == 0;
+  if (lead) SSD_PHASE(1, b, 0);
   // wave 0, lane j < K: drafted token, sigma_j(x_j), the target logit at x_j
   // captured by the streaming pass; lane j <= K: the draft row statistics;
   // thread t < (K+1) F: entry t of the draft top-F lists of all K + 1 rows
@@ -938,6 +967,7 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
   }
   if (tf_lds && tid < K1 * F) sm.tf[tid] = tfv;
   __syncthreads();
+  if (lead) SSD_PHASE(1, b, 1);  // prologue loads and the K+1 rows' statistics
   // argmax of the T > 0 rows is only needed for the optional statistics
   if (lead && !greedy && p.stats) {
     for (int j = wave; j < K1; j += ENW) {
@@ -1001,6 +1031,7 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     st.argmax = sm.vam[tid];
     p.stats[r0 + tid] = st;
   }
+  if (lead) SSD_PHASE(1, b, 2);  // acceptance decisions
   if (greedy) return;
   __syncthreads();
   const int ks = sm.ks;
@@ -1091,6 +1122,7 @@ __device__ __forceinline__ void accept_residual(const Params& p, int b, int chun
     residual(ut0, ud0, be0, Mt0);
     if (be1 < end) residual(ut1, ud1, be1, Mt1);
   }
+  if (lead) SSD_PHASE(1, b, 3);  // this chunk's residual block sums
 }
 
 template <int DT, bool AL>
@@ -1120,9 +1152,11 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
       S[k] = in ? v[k].y : 0.f;
     }
   }
+  SSD_PHASE(2, b, 1);  // residual block sums in hand
   int beta = block_stage(NB, p.seed, b, ks, ST_BONUS_BLOCK, sm.ru[0], [&](int, int k) -> float {
     return any ? R[k] : block_w(M[k], S[k], mt, s);
   });
+  SSD_PHASE(2, b, 2);  // block drawn
   if (beta < 0) beta = 0;
   const int x0 = beta * BLK + TPT * tid;
   Run<DT, AL> runt, rund;
@@ -1134,6 +1168,7 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
   run_finish<DT, AL>(V, x0, runt, zt);
   run_finish<DT, AL>(V, x0, rund, zd);
   const float Mb = sm.M[beta];
+  SSD_PHASE(2, b, 3);  // chosen block of both rows re-read
   int x = -1;
   if (any) {
     // r = p - sigma > 0 iff d = ln sigma - ln p < 0, and then r = p (-expm1(d))
@@ -1155,6 +1190,7 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
       return zt[e] > -INFINITY ? (Mb - zt[e]) * s : INFINITY;
     });
   }
+  SSD_PHASE(2, b, 4);  // token race
   if (tid == 0) {
     p.bonus[b] = (x >= 0 && x < V) ? x : 0;
     sm.bonus = (x >= 0 && x < V) ? x : 0;
@@ -1416,6 +1452,7 @@ __device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k,
 template <int DT, bool AL>
 __device__ __forceinline__ void residual_item(const Params& p, int b, ESm& sm) {
   const int NB = p.NB;
+  SSD_PHASE(2, b, 0);
   // the residual sums (used only when the state asks for them), the state,
   // and the outcome of sequences decided earlier are loaded together
   // (unconditional loads from clamped addresses: all in flight at once)
@@ -1446,6 +1483,7 @@ __device__ __forceinline__ void residual_item(const Params& p, int b, ESm& sm) {
   } else if (threadIdx.x < 64) {
     cache_lookup_wave(p, b, ks0, y0, cr);
   }
+  SSD_PHASE(2, b, 5);  // cache lookup
 }
 
 template <int DT, bool AL>

@@ -760,6 +760,17 @@ ssd_status ssd_read_probe(const void* buf, size_t bytes, int32_t variant, uint32
   return hip_status(hipGetLastError());
 }
 
+ssd_status ssd_phase_read(int32_t kind, uint64_t* out, int64_t n) {
+  if (kind < 0 || kind > 2 || !out || n < 0 || n > (int64_t)PH_ITEMS * PH_N) return SSD_ERR_INVALID_ARG;
+#ifdef SSD_PHASES
+  const hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_phase), (size_t)n * sizeof(uint64_t),
+                                           (size_t)kind * PH_ITEMS * PH_N * sizeof(uint64_t));
+  return hip_status(e);
+#else
+  return SSD_ERR_UNSUPPORTED;
+#endif
+}
+
 ssd_status ssd_timer_enable(int32_t max_launches) {
   if (max_launches < 0 || max_launches > (1 << 20)) return SSD_ERR_INVALID_ARG;
   timer_free();

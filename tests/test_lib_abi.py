@@ -326,3 +326,16 @@ def test_verify_tree_rejects_bad_arguments(L):
     assert f(ctypes.byref(args(ok, wsb=64)), None) == 3
     assert ssd.workspace_bytes(ssd.OP_VERIFY_TREE, 2, 3, 100) > 0
     assert ssd.workspace_bytes(ssd.OP_VERIFY_TREE, 2, 64, 100) == 0
+
+
+def test_phase_read_is_off_in_the_ordinary_build(L):
+    """ssd_phase_read only serves the instrumented build; the ordinary
+    library checks its arguments and then reports SSD_ERR_UNSUPPORTED."""
+    f = L.ssd_phase_read
+    f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64]
+    buf = (ctypes.c_uint64 * 8)()
+    assert f(3, buf, 8) == 1
+    assert f(0, None, 8) == 1
+    assert f(0, buf, -1) == 1
+    assert f(0, buf, 8192 * 8 + 1) == 1
+    assert f(0, buf, 8) == 2
