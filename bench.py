@@ -164,9 +164,10 @@ def phases(a):
     lossless_verify_sample_amd.build --phases`): the workload's sampling and
     verification as separate calls, with the cache step, a few times; then
     per phase the median, 90th percentile and maximum over the items of the
-    last call (rows for the sampling epilogue, sequences for acceptance and
-    bonus), in microseconds, and the spread from the first item's start to
-    the last item's end.  Prints one JSON line."""
+    last call (rows for the sampling epilogue, sequences with a residual for
+    the verification kernel), in microseconds, the spread from the first
+    item's start to the last item's end, and the number of blocks the lazy
+    block race evaluated.  Prints one JSON line.""" 
     import numpy as np
     import torch
 
@@ -188,16 +189,14 @@ def phases(a):
     acc = v["accept_len"].cpu().numpy()
     names = {0: ["partials loaded, row maximum", "block weights summed", "top-F list",
                  "sigma normaliser and outputs", "block drawn", "chosen block re-read, token drawn"],
-             1: ["K+1 rows' statistics", "acceptance decisions", "residual sums of the chunk"],
-             2: ["residual sums in hand", "block drawn", "chosen block re-read", "token drawn", "cache lookup"]}
-    items = {0: B * (K + 1), 1: B, 2: B}
+             1: ["K+1 rows' statistics", "acceptance decisions", "lazy block race", "bonus token", "cache lookup"]}
+    items = {0: B * (K + 1), 1: B}
     Tb = T.cpu().numpy()
     keep = {0: (np.arange(B * (K + 1)) % (K + 1) < K) & (np.repeat(Tb, K + 1) > 0),  # sampled rows
-            1: (acc < K) & (Tb > 0),                                  # sequences with a residual
-            2: (acc < K) & (Tb > 0)}
+            1: (acc < K) & (Tb > 0)}                                  # sequences with a residual
     out = {"metric": "phase timings of the latency-bound kernels", "unit": "us", "config": cfg.name,
            "B": B, "K": K, "V": V, "cache_fanout": Fk}
-    for kind in (0, 1, 2):
+    for kind in (0, 1):
         st = ssd.phase_read(kind, items[kind])[keep[kind]]
         n = len(names[kind])
         ph = {}
@@ -206,10 +205,15 @@ def phases(a):
             ph[names[kind][k]] = {"median": round(float(np.median(dd)), 3), "p90": round(float(np.percentile(dd, 90)), 3),
                                   "max": round(float(dd.max()), 3)}
         tot = (st[:, n] - st[:, 0]) * 0.01
-        out[["sampling_epilogue", "acceptance_pass", "bonus"][kind]] = {
-            "items": int(len(st)), "phases": ph,
-            "item_total": {"median": round(float(np.median(tot)), 3), "max": round(float(tot.max()), 3)},
-            "first_start_to_last_end": round(float((st[:, n].max() - st[:, 0].min()) * 0.01), 3)}
+        rec = {"items": int(len(st)), "phases": ph,
+               "item_total": {"median": round(float(np.median(tot)), 3), "max": round(float(tot.max()), 3)},
+               "first_start_to_last_end": round(float((st[:, n].max() - st[:, 0].min()) * 0.01), 3)}
+        if kind == 1:
+            # slot 7: blocks the lazy race evaluated per sequence
+            ev = st[:, 7]
+            rec["blocks_evaluated"] = {"mean": round(float(ev.mean()), 3), "p90": float(np.percentile(ev, 90)),
+                                       "max": int(ev.max()), "row_blocks": int((V + 2047) // 2048)}
+        out[["sampling_epilogue", "verification"][kind]] = rec
     print(json.dumps(out), flush=True)
 
 

@@ -503,11 +503,10 @@ ssd_status ssd_read_probe(const void* buf, size_t bytes, int32_t variant, uint32
  *   kind 0: sampling epilogue, item = row b*(K+1)+j: start, partials loaded,
  *           block weights summed, top-F list, sigma normaliser and outputs,
  *           block drawn, token drawn;
- *   kind 1: acceptance and residual pass, item = sequence (its first chunk's
- *           workgroup): start, statistics of the K+1 rows, decisions, the
- *           chunk's residual sums;
- *   kind 2: bonus and lookup, item = sequence: start, residual sums in hand,
- *           block drawn, chosen block re-read, token drawn, lookup done.
+ *   kind 1: verification after the streaming pass, item = sequence: start,
+ *           statistics of the K+1 rows, decisions, block of the bonus drawn
+ *           (the lazy block race), bonus token, lookup done; slot 7 holds
+ *           the number of blocks the lazy race evaluated (not a time).
  * ssd_phase_read copies the first n stamps of `kind` (item * 8 + slot, up to
  * 8192 items; slots an item does not reach keep older values) to host `out`.
  * Errors: SSD_ERR_UNSUPPORTED in the ordinary build; SSD_ERR_INVALID_ARG for

@@ -347,6 +347,17 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
   return umin64(umin64(rl_u64(x, 0), rl_u64(x, 16)), umin64(rl_u64(x, 32), rl_u64(x, 48)));
 }
 
+// Workgroup barrier for exchanges through LDS: the fences order LDS accesses
+// only, so the barrier does not wait for outstanding global loads and stores
+// as __syncthreads does (a store still in flight costs a round trip to
+// memory there).  Every exchange between the threads of a workgroup in these
+// kernels goes through LDS.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // workgroup reductions for the epilogue kernels (EWG threads; every thread
 // calls and gets the result, combined in a fixed order).  Each call site
@@ -357,7 +368,7 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
 __device__ __forceinline__ float wg_max(float x, float* slot) {
   x = wave_max(x);
   if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_sync();
   float m = slot[0];
 #pragma unroll
   for (int k = 1; k < ENW; ++k) m = fmaxf(m, slot[k]);
@@ -366,7 +377,7 @@ __device__ __forceinline__ float wg_max(float x, float* slot) {
 __device__ __forceinline__ double wg_sum_d(double x, double* slot) {
   x = wave_sum_d(x);
   if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_sync();
   double t = slot[0];
 #pragma unroll
   for (int k = 1; k < ENW; ++k) t += slot[k];
@@ -375,7 +386,7 @@ __device__ __forceinline__ double wg_sum_d(double x, double* slot) {
 __device__ __forceinline__ uint64_t wg_min_u64(uint64_t x, uint64_t* slot) {
   x = wave_min_u64(x);
   if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_sync();
   uint64_t m = slot[0];
 #pragma unroll
   for (int k = 1; k < ENW; ++k) m = umin64(m, slot[k]);
@@ -384,7 +395,7 @@ __device__ __forceinline__ uint64_t wg_min_u64(uint64_t x, uint64_t* slot) {
 __device__ __forceinline__ uint64_t wg_max_u64(uint64_t x, uint64_t* slot) {
   x = wave_max_u64(x);
   if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_sync();
   uint64_t m = slot[0];
 #pragma unroll
   for (int k = 1; k < ENW; ++k) m = umax64(m, slot[k]);
@@ -393,7 +404,7 @@ __device__ __forceinline__ uint64_t wg_max_u64(uint64_t x, uint64_t* slot) {
 __device__ __forceinline__ int wg_min_i(int x, int* slot) {
   x = wave_min_i(x);
   if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_sync();
   int m = slot[0];
 #pragma unroll
   for (int k = 1; k < ENW; ++k) m = min(m, slot[k]);

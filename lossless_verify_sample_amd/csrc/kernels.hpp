@@ -26,28 +26,42 @@ namespace ssd {
 // Phase stamps of the latency-bound kernels, compiled in only for the
 // instrumented build (-DSSD_PHASES, a measurement aid): the first lane of
 // wave 0 records the 100 MHz real-time counter at fixed points of each item
-// (kind 0: sampling epilogue, per row; kind 1: acceptance and residual pass,
-// the first chunk of each sequence; kind 2: bonus and cache lookup, per
-// sequence).
+// (kind 0: sampling epilogue, per row; kind 1: verification after the
+// streaming pass, per sequence).
 constexpr int PH_N = 8;
 constexpr int PH_ITEMS = 8192;
 #ifdef SSD_PHASES
-__device__ uint64_t g_phase[3][PH_ITEMS * PH_N];
+__device__ uint64_t g_phase[2][PH_ITEMS * PH_N];
 #define SSD_PHASE(kind, item, k)                                                              \
   do {                                                                                        \
     if (threadIdx.x == 0 && (int64_t)(item) < PH_ITEMS)                                       \
       g_phase[kind][(int64_t)(item) * PH_N + (k)] = __builtin_amdgcn_s_memrealtime();          \
   } while (0)
+// Buffered stamps (verification): kept in registers and stored at the end
+// of the item, so that no stamp's store is outstanding while the item waits
+// on a load (the wait counter counts stores too).
+#define SSD_PH_DECL uint64_t ph_[PH_N] = {}
+#define SSD_PH(k) (ph_[k] = __builtin_amdgcn_s_memrealtime())
+#define SSD_PH_SET(k, v) (ph_[k] = (uint64_t)(v))
+#define SSD_PH_FLUSH(kind, item)                                             \
+  do {                                                                       \
+    if (threadIdx.x == 0 && (int64_t)(item) < PH_ITEMS)                      \
+      for (int k_ = 0; k_ < PH_N; ++k_) g_phase[kind][(int64_t)(item) * PH_N + k_] = ph_[k_]; \
+  } while (0)
 #else
 #define SSD_PHASE(kind, item, k) \
   do {                           \
   } while (0)
+#define SSD_PH_DECL do {} while (0)
+#define SSD_PH(k) do {} while (0)
+#define SSD_PH_SET(k, v) do {} while (0)
+#define SSD_PH_FLUSH(kind, item) do {} while (0)
 #endif
 
 enum Mode { M_SOFTMAX = 0, M_TOPF = 1, M_SAMPLE = 2, M_VERIFY = 3 };
 
 constexpr int CH = 8;             // blocks per workgroup in the streaming pass (2 per wave)
-constexpr int CH_R = 2 * EWG / 64;  // blocks per workgroup in the residual pass (2 per wave)
+constexpr int CH_R = 2 * EWG / 64;  // blocks per pass of a workgroup over a residual (2 per wave)
 constexpr int TPT = BLK / EWG;    // tokens per epilogue thread in a token stage
 constexpr int NBT = MAX_NB / EWG; // blocks per epilogue thread
 constexpr int NBL = MAX_NB / 64;  // blocks per lane when a wave holds a whole row
@@ -55,7 +69,7 @@ static_assert(TPT == 8 && NBT == 2, "epilogue layout assumes 256 threads over 20
 constexpr int KTH_ROUNDS = 8;     // top-F threshold by maximum rounds up to this F, by radix search above
 constexpr int TF_CAP = EWG;       // (K+1)*F draft top-F entries prefetched into LDS when they fit
 
-// What verification hands to the residual pass for one sequence.
+// Constants of the bonus draw from the residual of one sequence's row k*.
 struct SeqState {
   int need;      // 1: bonus from the residual at row kstar (T > 0, kstar < K)
   int kstar;
@@ -76,7 +90,6 @@ struct Params {
   int64_t V, ld;            // ld in elements
   int64_t rows;             // rows streamed by the kernel
   int NB, nchunk;           // blocks per row, workgroups per row
-  int racc;                 // verification: blocks per workgroup of the residual pass (a multiple of CH_R)
   int jlo, jn;              // jn > 0: the streaming pass covers positions jlo .. jlo + jn - 1 of every sequence
   int early;                // verification: rows past the first rejection may not have been streamed
   int keep;                 // verification: positions < keep are streamed with ordinary (cached) loads
@@ -101,8 +114,6 @@ struct Params {
   int32_t* acc_len;
   int32_t* bonus;
   float* p_out;
-  SeqState* state;
-  float2* rpart;            // residual block sums and target block maxima [B, NB]
   // speculation cache (optional): depth offsets, keys, payload, lookup outputs
   int koff[MAX_K1 + 1];
   int Bgt;
@@ -433,7 +444,7 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
   // general case: wave 0 lists the candidate blocks, the blocks to re-read
   // and the one-element candidates; then every thread scans its 16-byte
   // chunks of the re-read blocks, RB blocks' loads in flight at a time
-  __syncthreads();
+  lds_sync();
   const uint64_t below = (1ull << lane) - 1ull;
   int n1 = 0, ncb = 0, nrb = 0;
 #pragma unroll
@@ -450,7 +461,7 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
     n1 += __popcll(om);
     nrb += __popcll(rm);
   }
-  __syncthreads();
+  lds_sync();
   {
     constexpr int VW = Dt<DT>::VW, RB = 8;
     for (int c0 = tid; c0 < BLK / VW; c0 += EWG) {  // chunk c0 of every re-read block
@@ -495,7 +506,7 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
       }
     }
   }
-  __syncthreads();
+  lds_sync();
   const int n = n1 + sm.nre;
   if (n <= CAND_CAP) {
     for (int c = tid; c < n; c += EWG) {
@@ -534,7 +545,7 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
       prev = best;
     }
   }
-  __syncthreads();
+  lds_sync();
   return lane < Fs ? sm.tkey[lane] : 0ull;
 }
 
@@ -870,272 +881,104 @@ __device__ __forceinline__ void epi_keys_p(const Params& p, int item, ESm& sm) {
   if (lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = (int)key_idx(tk);  // wave 0: Fj <= 64
 }
 
-// Acceptance and residual pass of verification, one workgroup per (sequence,
-// chunk of CH_R blocks).  Every workgroup of a sequence merges the partials
-// of its K + 1 target rows and takes the acceptance decisions itself (the
-// same arithmetic in each, so all agree on k*); this costs a few KB of L2
-// reads per workgroup and saves a kernel boundary and a dependent load.
-// Chunk 0 writes the per-sequence outputs and, when every draft token is
-// accepted or the sequence is greedy, the bonus token.  When T > 0 and k* <
-// K each workgroup adds the residual block sums of its chunk: sums of
-// max(0, p - sigma) over target row k* and draft row k*, in the target's
-// units scaled by exp(L_t) 2^(eps_t) (a constant per sequence), with the
-// target block maxima.
-template <int DT, bool AL, int PLN>
-__device__ __forceinline__ void accept_residual(const Params& p, int b, int chunk, ESm& sm) {
-  const int K = p.K, K1 = K + 1, NB = p.NB, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int V = (int)p.V;
-  const float T = p.temp[b];
-  const bool greedy = !(T > 0.f);
-  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
-  const double invT = greedy ? 0.0 : 1.0 / (double)T;
-  const int64_t r0 = (int64_t)b * K1;
-  const int64_t rs = p.ld * Dt<DT>::SZ;
-  const bool lead = chunk == 0;
-  if (lead) SSD_PHASE(1, b, 0);
-  // wave 0, lane j < K: drafted token, sigma_j(x_j), the target logit at x_j
-  // captured by the streaming pass; lane j <= K: the draft row statistics;
-  // thread t < (K+1) F: entry t of the draft top-F lists of all K + 1 rows
-  // (the residual of row k* needs one).  All loaded unconditionally from
-  // clamped indices (a valid stand-in array when K = 0 or F = 0: the
-  // captured-logit workspace), so that they and the partials below are in
-  // flight together (a load under a branch gets a wait of its own) and no
-  // load waits on k*.
-  const int F = p.F;
-  const bool tf_lds = F > 0 && K1 * F <= TF_CAP;
-  const int tq = min(tid, max(K - 1, 0));
-  const int32_t* dtok = K > 0 ? p.dtok : reinterpret_cast<const int32_t*>(p.zcap);
-  const float* dqp = K > 0 ? p.dq : p.zcap;
-  const int xl = dtok[b * K + tq];
-  const float ql = dqp[b * K + tq], zl = p.zcap[b * K + tq];
-  const ssd_row_stats ds = p.dstats[r0 + min(tid, K)];
-  const int tt = tf_lds ? min(tid, K1 * F - 1) : 0;
-  const int32_t* tfp = tf_lds ? p.dtopf + (r0 + tt / F) * p.ld_dtopf + tt % F : reinterpret_cast<const int32_t*>(p.zcap);
-  const int tfv = *tfp;
-  const int xj = tid < K ? xl : -1;
-  const float qj = tid < K ? ql : 0.f, ztj = tid < K ? zl : 0.f;
-  const float dmax = (tid <= K && !greedy) ? ds.max : 0.f;
-  const double dlse = (tid <= K && !greedy) ? (double)ds.lse : 0.0;
-  // row statistics: wave w merges rows j = w, w + ENW, ..., two rows per pass
-  // with both rows' loads in flight
-  auto merge = [&](const WRow<PLN>& r, int j) {
-    float lm = r.M[0];
+// Residual block sum sum_x max(0, p_x - c sigma_x) over block be of one row,
+// in the target's units (one wave; every lane gets the sum).  ut and ud hold
+// the block of the target and draft rows; e1 = 2^(z_t s + ot) and e2 =
+// 2^(z_d s + od); nk = -c times the draft term in the target's units and nkc
+// = nk C for the members of the draft's top-F set (tfl: F entries, in LDS or
+// global memory), whose terms are corrected one by one.  The member's logits
+// are element kk of lane gi & 63 in the wave's registers.
+template <int DT, bool AL>
+__device__ __forceinline__ float block_residual(const RawBlock<DT, AL>& ut, const RawBlock<DT, AL>& ud, int be, int V,
+                                                float s, float ot, float od, float nk, float nkc, int F,
+                                                const int32_t* tfl) {
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
-    const float m = wave_max(lm);
-    int fb = -1, am = -1;
-    double wsum = 0.0;
+  for (int k = 0; k < 32; k += 2) {
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k), s, ot));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k), s, od));
+    const float f1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k + 1), s, ot));
+    const float f2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k + 1), s, od));
+    a0 += fmaxf(fmaf(nk, e2, e1), 0.f);
+    a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
+  }
+  float R = wave_sum(a0 + a1);
+  for (int f = 0; f < F; ++f) {
+    const int x = __builtin_amdgcn_readfirstlane(tfl[f]);
+    if (x >= 0 && x < V && x / BLK == be) {
+      constexpr int VW = Dt<DT>::VW;
+      const int off = x - be * BLK, gi = off / VW, kk = (gi >> 6) * VW + off % VW;
+      float zt = raw_elem<DT, AL>(ut, 0), zd = raw_elem<DT, AL>(ud, 0);
 #pragma unroll
-    for (int i = PLN - 1; i >= 0; --i) {
-      if (!greedy) wsum += (double)block_w(r.M[i], r.S[i], m, s);
-      const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
-      if (mk) {
-        fb = 64 * i + (int)__builtin_ctzll(mk);
-        am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
+      for (int k = 1; k < 32; ++k) {
+        zt = k == kk ? raw_elem<DT, AL>(ut, k) : zt;
+        zd = k == kk ? raw_elem<DT, AL>(ud, k) : zd;
       }
-    }
-    wsum = wave_sum_d(wsum);
-    if (lead && j == K) {
-#pragma unroll
-      for (int i = 0; i < PLN; ++i) {
-        const int be = lane + 64 * i;
-        if (be < NB) {
-          sm.M[be] = r.M[i];
-          sm.S[be] = r.S[i];
-        }
-      }
-    }
-    if (lane == 0) {
-      sm.vm[j] = m;
-      sm.vL[j] = greedy ? 0.0 : ln_fast(wsum);
-      sm.vfb[j] = fb < 0 ? 0 : fb;                  // (a NaN row matches no block)
-      sm.vam[j] = greedy ? (am < 0 ? 0 : am) : -1;  // greedy rows carry the block argmax in their partial
-    }
-  };
-  float uacc = 0.f;
-  for (int j0 = wave; j0 < K1; j0 += 2 * ENW) {
-    const int j1 = j0 + ENW;
-    WRow<PLN> ra, rb;
-    load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
-    load_wrow<PLN>(p.part + (r0 + min(j1, K)) * NB, NB, rb);
-    // wave 0, lane j: the acceptance draw u_j, computed while the partials load
-    if (wave == 0 && j0 == 0 && !greedy)
-      uacc = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
-    merge(ra, j0);
-    if (j1 < K1) merge(rb, j1);
-  }
-  if (tf_lds && tid < K1 * F) sm.tf[tid] = tfv;
-  __syncthreads();
-  if (lead) SSD_PHASE(1, b, 1);  // prologue loads and the K+1 rows' statistics
-  // argmax of the T > 0 rows is only needed for the optional statistics
-  if (lead && !greedy && p.stats) {
-    for (int j = wave; j < K1; j += ENW) {
-      const int am = wave_first_eq<DT, AL>(p.x + (r0 + j) * rs, V, sm.vfb[j], sm.vm[j]);
-      if (lane == 0) sm.vam[j] = am;
-    }
-    __syncthreads();
-  }
-  // acceptance decisions (wave 0, lane j < K) and p_j(x_j) for every position
-  if (wave == 0) {
-    bool acc = false;
-    double pj = 0.0;
-    if (lane < K && xj >= 0 && xj < V) {
-      if (greedy) {
-        acc = (xj == sm.vam[lane]);
-        pj = acc ? 1.0 : 0.0;
-      } else {
-        pj = exp_fast(((double)ztj - (double)sm.vm[lane]) * invT - sm.vL[lane]);
-        const double q = (double)qj;
-        const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
-        acc = (double)uacc < rho;
-      }
-    }
-    const uint64_t rej = __ballot(lane < K && !acc);
-    const int ks = rej ? (int)__builtin_ctzll(rej) : K;
-    // (early exit: the rows past k* may not have been read)
-    if (lead && lane < K) p.p_out[b * K + lane] = (p.early && lane > ks) ? __builtin_nanf("") : (float)pj;
-    SeqState ss{};
-    if (!greedy && ks < K) {
-      // hand-over to the residual pass (values of target and draft row k*)
-      const float mt = sm.vm[ks];
-      const float md = rl_f(dmax, ks);
-      const double Ld = rl_d(dlse, ks), Lt = sm.vL[ks];
-      ss.need = 1;
-      ss.kstar = ks;
-      ss.s = s;
-      ss.m_t = mt;
-      ss.o_t = -mt * s;
-      ss.o_d = -md * s;
-      const double et = (double)ss.o_t + (double)mt * (double)s;
-      const double ed = (double)ss.o_d + (double)md * (double)s;
-      ss.invT = invT;
-      ss.D0 = ((double)mt - (double)md) * invT + Lt - Ld;
-      ss.lnC = ln_fast((double)p.C);
-      ss.kf = (float)exp_fast((et - ed) * LN2 + (Lt - Ld));
-    }
-    if (lane == 0) {
-      sm.ks = ks;
-      sm.ss = ss;
-      if (lead) {
-        p.acc_len[b] = ks;
-        p.state[b] = ss;
-        if (greedy) p.bonus[b] = sm.vam[ks];
-      }
+      zt = rl_f(zt, gi & 63);
+      zd = rl_f(zd, gi & 63);
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(zt, s, ot));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(zd, s, od));
+      R += fmaxf(fmaf(nkc, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
     }
   }
-  if (lead && p.stats && tid < K1) {
-    ssd_row_stats st;
-    st.lse = sm.vL[tid];
-    st.max = sm.vm[tid];
-    st.argmax = sm.vam[tid];
-    p.stats[r0 + tid] = st;
-  }
-  if (lead) SSD_PHASE(1, b, 2);  // acceptance decisions
-  if (greedy) return;
-  __syncthreads();
-  const int ks = sm.ks;
-  if (ks == K) {
-    if (!lead) return;
-    // all K accepted: bonus ~ p_K (row K's partials are in sm.M / sm.S)
-    const float m = sm.vm[K];
-    int beta = block_stage(NB, p.seed, b, K, ST_BONUS_BLOCK, sm.ru[0], [&](int be, int) -> float {
-      return block_w(sm.M[be], sm.S[be], m, s);
-    });
-    if (beta < 0) beta = 0;
-    const unsigned char* rp = p.x + (r0 + K) * rs;
-    const int x0 = beta * BLK + TPT * tid;
-    Run<DT, AL> run;
-    run_issue<DT, AL>(rp, V, x0, run);
-    const RaceWords rw = race_words(x0, p.seed, b, K, ST_BONUS_TOKEN);  // while the block loads
-    __builtin_amdgcn_sched_barrier(0);
-    float z[TPT];
-    run_finish<DT, AL>(V, x0, run, z);
-    const float Mb = sm.M[beta];
-    const int x = token_race(x0, V, rw, sm.ru[1], [&](int e) -> float {
-      return z[e] > -INFINITY ? (Mb - z[e]) * s : INFINITY;
-    });
-    if (tid == 0) p.bonus[b] = x >= 0 ? x : 0;
-    return;
-  }
-  // residual block sums of this chunk's blocks, CH_R at a time (two per
-  // wave, all their loads in flight together)
-  const SeqState ss = sm.ss;
-  const int64_t row = r0 + ks;
-  const unsigned char* rt = p.x + row * rs;
-  const unsigned char* rd = p.xd + row * rs;
-  const float ot = ss.o_t, od = ss.o_d, nk = -ss.kf;
-  const int64_t rrow = row * p.ld_dtopf;
-  // the target block maxima of row k* come from its streaming partials
-  const float4* tpart = p.part + (r0 + ks) * NB;
-  auto residual = [&](const RawBlock<DT, AL>& ut, const RawBlock<DT, AL>& ud, int be, float Mt) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < 32; k += 2) {
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k), s, ot));
-      const float e2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k), s, od));
-      const float f1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k + 1), s, ot));
-      const float f2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k + 1), s, od));
-      a0 += fmaxf(fmaf(nk, e2, e1), 0.f);
-      a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
-    }
-    float R = wave_sum(a0 + a1);
-    // members of the draft's top-F set in this block carry the factor C; the
-    // member's logits are element kk of lane gi & 63 in this wave's registers
-    for (int f = 0; f < F; ++f) {
-      const int x = __builtin_amdgcn_readfirstlane(tf_lds ? sm.tf[ks * F + f] : p.dtopf[rrow + f]);
-      if (x >= 0 && x < V && x / BLK == be) {
-        constexpr int VW = Dt<DT>::VW;
-        const int off = x - be * BLK, gi = off / VW, kk = (gi >> 6) * VW + off % VW;
-        float zt = raw_elem<DT, AL>(ut, 0), zd = raw_elem<DT, AL>(ud, 0);
-#pragma unroll
-        for (int k = 1; k < 32; ++k) {
-          zt = k == kk ? raw_elem<DT, AL>(ut, k) : zt;
-          zd = k == kk ? raw_elem<DT, AL>(ud, k) : zd;
-        }
-        zt = rl_f(zt, gi & 63);
-        zd = rl_f(zd, gi & 63);
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(zt, s, ot));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(zd, s, od));
-        R += fmaxf(fmaf(nk * p.C, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
-      }
-    }
-    if (lane == 0) p.rpart[(int64_t)b * NB + be] = make_float2(fmaxf(R, 0.f), Mt);
-  };
-  const int end = min(NB, (chunk + 1) * p.racc);
-  for (int base = chunk * p.racc; base < end; base += CH_R) {
-    const int be0 = base + wave, be1 = be0 + ENW;
-    if (be0 >= end) break;
-    RawBlock<DT, AL> ut0, ud0, ut1, ud1;
-    if ((base + CH_R) * BLK <= V) {
-      load_raw<DT, AL, true>(rt, V, be0, lane, ut0);
-      load_raw<DT, AL, true>(rd, V, be0, lane, ud0);
-      load_raw<DT, AL, true>(rt, V, be1, lane, ut1);
-      load_raw<DT, AL, true>(rd, V, be1, lane, ud1);
-    } else {
-      load_raw<DT, AL, false>(rt, V, be0, lane, ut0);
-      load_raw<DT, AL, false>(rd, V, be0, lane, ud0);
-      load_raw<DT, AL, false>(rt, V, min(be1, NB - 1), lane, ut1);
-      load_raw<DT, AL, false>(rd, V, min(be1, NB - 1), lane, ud1);
-    }
-    const float Mt0 = tpart[be0].x, Mt1 = tpart[min(be1, NB - 1)].x;
-    residual(ut0, ud0, be0, Mt0);
-    if (be1 < end) residual(ut1, ud1, be1, Mt1);
-  }
-  if (lead) SSD_PHASE(1, b, 3);  // this chunk's residual block sums
+  return fmaxf(R, 0.f);
 }
 
+// Token stage of the bonus drawn from row k*'s residual inside block beta
+// (every thread calls; returns the token, -1 if none): r_x = p_x (-expm1(d_x))
+// with d_x = ln(c sigma_x) - ln p_x formed in fp64 from the logits (D0 holds
+// the constant part), or p_x itself when the row has no residual mass (any =
+// false) or the chosen block had mass only through rounding.  Mb: the target
+// block maximum of beta; tfl: row k*'s draft top-F list (F entries).
 template <int DT, bool AL>
-__device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqState& ss, const float (&R)[NBT],
-                                            const float (&Mt)[NBT], bool tf_lds, ESm& sm) {
-  const int tid = threadIdx.x, K1 = p.K + 1, NB = p.NB, V = (int)p.V, F = p.F;
+__device__ __forceinline__ int residual_token(const Params& p, int b, const SeqState& ss, int beta, float Mb,
+                                              bool any, const int32_t* tfl, uint64_t* slot_r, uint64_t* slot_p) {
+  const int tid = threadIdx.x, K1 = p.K + 1, V = (int)p.V, F = p.F;
   const int ks = ss.kstar;
   const int64_t row = (int64_t)b * K1 + ks;
   const int64_t rs = p.ld * Dt<DT>::SZ;
   const unsigned char* rt = p.x + row * rs;
   const unsigned char* rd = p.xd + row * rs;
+  const float s = ss.s;
+  const int x0 = beta * BLK + TPT * tid;
+  Run<DT, AL> runt, rund;
+  run_issue<DT, AL>(rt, V, x0, runt);
+  run_issue<DT, AL>(rd, V, x0, rund);
+  const RaceWords rw = race_words(x0, p.seed, b, ks, ST_BONUS_TOKEN);  // while the blocks load
+  __builtin_amdgcn_sched_barrier(0);
+  float zt[TPT], zd[TPT];
+  run_finish<DT, AL>(V, x0, runt, zt);
+  run_finish<DT, AL>(V, x0, rund, zd);
+  int x = -1;
+  if (any) {
+    // r = p - c sigma > 0 iff d = ln(c sigma) - ln p < 0, and then r = p (-expm1(d))
+    const uint32_t smask = F <= 0 ? 0u : set_mask(tfl, F, x0);
+    const double invT = ss.invT, D0 = ss.D0, lnC = ss.lnC;
+    x = token_race(x0, V, rw, slot_r, [&](int e) -> float {
+      if (!(zt[e] > -INFINITY)) return INFINITY;
+      const float tp = (Mb - zt[e]) * s;
+      if (!(zd[e] > -INFINITY)) return tp;
+      const double dd = ((double)zd[e] - (double)zt[e]) * invT + D0 + (((smask >> e) & 1u) ? lnC : 0.0);
+      if (!(dd < 0.0)) return INFINITY;
+      return tp - __builtin_amdgcn_logf(-expm1f((float)dd));
+    });
+  }
+  if (x < 0) {
+    x = token_race(x0, V, rw, slot_p, [&](int e) -> float {
+      return zt[e] > -INFINITY ? (Mb - zt[e]) * s : INFINITY;
+    });
+  }
+  return x;
+}
+
+// Bonus from the residual given its block sums R (thread-owned blocks t +
+// k*EWG) and the target row's block maxima Mt (token-tree verification).
+template <int DT, bool AL>
+__device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqState& ss, const float (&R)[NBT],
+                                            const float (&Mt)[NBT], ESm& sm) {
+  const int tid = threadIdx.x, K1 = p.K + 1, NB = p.NB, F = p.F;
+  const int64_t row = (int64_t)b * K1 + ss.kstar;
   const float s = ss.s, mt = ss.m_t;
-  // residual block sums with the target row's block maxima
 #pragma unroll
   for (int k = 0; k < NBT; ++k)
     if (tid + k * EWG < NB) sm.M[tid + k * EWG] = Mt[k];
@@ -1152,226 +995,16 @@ __device__ __forceinline__ void epi_residual(const Params& p, int b, const SeqSt
       S[k] = in ? v[k].y : 0.f;
     }
   }
-  SSD_PHASE(2, b, 1);  // residual block sums in hand
-  int beta = block_stage(NB, p.seed, b, ks, ST_BONUS_BLOCK, sm.ru[0], [&](int, int k) -> float {
+  int beta = block_stage(NB, p.seed, b, ss.kstar, ST_BONUS_BLOCK, sm.ru[0], [&](int, int k) -> float {
     return any ? R[k] : block_w(M[k], S[k], mt, s);
   });
-  SSD_PHASE(2, b, 2);  // block drawn
   if (beta < 0) beta = 0;
-  const int x0 = beta * BLK + TPT * tid;
-  Run<DT, AL> runt, rund;
-  run_issue<DT, AL>(rt, V, x0, runt);
-  run_issue<DT, AL>(rd, V, x0, rund);
-  const RaceWords rw = race_words(x0, p.seed, b, ks, ST_BONUS_TOKEN);  // while the blocks load
-  __builtin_amdgcn_sched_barrier(0);
-  float zt[TPT], zd[TPT];
-  run_finish<DT, AL>(V, x0, runt, zt);
-  run_finish<DT, AL>(V, x0, rund, zd);
-  const float Mb = sm.M[beta];
-  SSD_PHASE(2, b, 3);  // chosen block of both rows re-read
-  int x = -1;
-  if (any) {
-    // r = p - sigma > 0 iff d = ln sigma - ln p < 0, and then r = p (-expm1(d))
-    const uint32_t smask = F <= 0 ? 0u : tf_lds ? set_mask(sm.tf + ks * F, F, x0)
-                                                : set_mask(p.dtopf + row * p.ld_dtopf, F, x0);
-    const double invT = ss.invT, D0 = ss.D0, lnC = ss.lnC;
-    x = token_race(x0, V, rw, sm.ru[1], [&](int e) -> float {
-      if (!(zt[e] > -INFINITY)) return INFINITY;
-      const float tp = (Mb - zt[e]) * s;
-      if (!(zd[e] > -INFINITY)) return tp;
-      const double dd = ((double)zd[e] - (double)zt[e]) * invT + D0 + (((smask >> e) & 1u) ? lnC : 0.0);
-      if (!(dd < 0.0)) return INFINITY;
-      return tp - __builtin_amdgcn_logf(-expm1f((float)dd));
-    });
-  }
-  if (x < 0) {
-    // no residual mass, or the chosen block had mass only through rounding: p there
-    x = token_race(x0, V, rw, sm.ru[2], [&](int e) -> float {
-      return zt[e] > -INFINITY ? (Mb - zt[e]) * s : INFINITY;
-    });
-  }
-  SSD_PHASE(2, b, 4);  // token race
+  const int32_t* tfl = F > 0 ? p.dtopf + row * p.ld_dtopf : nullptr;
+  const int x = residual_token<DT, AL>(p, b, ss, beta, sm.M[beta], any, tfl, sm.ru[1], sm.ru[2]);
   if (tid == 0) {
-    p.bonus[b] = (x >= 0 && x < V) ? x : 0;
-    sm.bonus = (x >= 0 && x < V) ? x : 0;
+    p.bonus[b] = (x >= 0 && x < (int)p.V) ? x : 0;
+    sm.bonus = (x >= 0 && x < (int)p.V) ? x : 0;
   }
-}
-
-// ---------------------------------------------------------------------------
-// kernels
-// ---------------------------------------------------------------------------
-// (f32 and unaligned rows need more registers per element: fewer waves)
-template <int DT, bool AL, int MODE>
-__device__ __forceinline__ void stream_item(const Params& p, int item) {
-  const int64_t it = item / p.nchunk;
-  const int chunk = item - (int)(it * p.nchunk);
-  const int64_t row = p.jn > 0 ? (it / p.jn) * (p.K + 1) + p.jlo + (it % p.jn) : it;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K1 = p.K + 1;
-  const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
-  const int V = (int)p.V, NB = p.NB;
-  const int b0 = chunk * CH + wave, b1 = b0 + NWAVE;
-  // the logit loads are issued first; the temperature (and the drafted
-  // token) are fetched behind them
-  RawBlock<DT, AL> r0, r1;
-  const bool full = (chunk + 1) * CH * BLK <= V;
-  // verification: the first p.keep target rows of a sequence, the likeliest
-  // rows of the first rejection, are read with ordinary loads so that the
-  // residual pass's re-read of row k* may find them in the Infinity Cache
-  const bool keep = MODE == M_VERIFY && (int)(row % K1) < p.keep;
-  if (full && keep) {
-    load_raw<DT, AL, true, false>(rp, V, b0, lane, r0);
-    load_raw<DT, AL, true, false>(rp, V, b1, lane, r1);
-  } else if (full) {
-    // every block of this chunk is full: all loads in flight together
-    load_raw<DT, AL, true>(rp, V, b0, lane, r0);
-    load_raw<DT, AL, true>(rp, V, b1, lane, r1);
-  } else {
-    // the chunk holding the ragged end of the row
-    load_raw<DT, AL, false>(rp, V, min(b0, NB - 1), lane, r0);
-    load_raw<DT, AL, false>(rp, V, min(b1, NB - 1), lane, r1);
-  }
-  float T = 0.f;
-  if constexpr (MODE == M_SOFTMAX) T = p.temp[row];
-  if constexpr (MODE == M_SAMPLE || MODE == M_VERIFY) T = p.temp[row / K1];
-  const double sd = LOG2E / (double)T;
-  const float s = (T > 0.f) ? (float)sd : 0.f;
-  int xj = -1;  // verification: drafted token of this target row (j < K)
-  if constexpr (MODE == M_VERIFY) {
-    const int j = (int)(row % K1);
-    if (j < p.K && p.dtok) xj = p.dtok[(row / K1) * p.K + j];
-  }
-  float v[32];
-  decode_raw<DT, AL>(r0, v);
-  const float4 P0 = block_partial<DT, MODE>(v, s, min(b0, NB - 1), lane);
-  decode_raw<DT, AL>(r1, v);
-  const float4 P1 = block_partial<DT, MODE>(v, s, min(b1, NB - 1), lane);
-  if (lane == 0 && b0 < NB) p.part[row * NB + b0] = P0;
-  if (lane == 0 && b1 < NB) p.part[row * NB + b1] = P1;
-  if constexpr (MODE == M_VERIFY) {
-    // the workgroup whose chunk holds x_j hands its target logit to the epilogue
-    if (xj >= 0 && xj < V && xj / (CH * BLK) == chunk && threadIdx.x == 0)
-      p.zcap[(row / K1) * p.K + (row % K1)] = load_elem<DT>(rp, xj);
-  }
-}
-
-template <int DT, bool AL, int MODE>
-__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(Params p) {
-  stream_item<DT, AL, MODE>(p, blockIdx.x);
-}
-
-// Early-exit verification.  A sequence's verification never reads target
-// rows past its first rejection, so once positions 0 .. J-1 have been
-// streamed, the rows from J on are needed only by sequences without a
-// rejection below J.  seq_alive judges that from the partials of rows < J
-// (written by the previous launch) conservatively: false only when some
-// position j < J is rejected with a clear margin (T > 0: u_j >= rho_j (1 +
-// 1e-4); greedy: x_j is not the row's argmax; or x_j outside [0, V)), so a
-// sequence that the acceptance pass may find unrejected below J is never
-// skipped.  Every thread calls; the result is uniform.
-struct GateSm {
-  float m[MAX_K1];
-  double L[MAX_K1];
-  int am[MAX_K1];
-  int alive;
-};
-template <int PLN>
-__device__ __forceinline__ bool seq_alive(const Params& p, int b, int J, GateSm& g) {
-  const int K = p.K, K1 = K + 1, NB = p.NB, V = (int)p.V;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float T = p.temp[b];
-  const bool greedy = !(T > 0.f);
-  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
-  const int Jd = min(J, K);  // positions with a decision
-  for (int j = wave; j < Jd; j += NWAVE) {
-    WRow<PLN> r;
-    load_wrow<PLN>(p.part + ((int64_t)b * K1 + j) * NB, NB, r);
-    float lm = r.M[0];
-#pragma unroll
-    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
-    const float m = wave_max(lm);
-    double ws = 0.0;
-    int am = -1;
-#pragma unroll
-    for (int i = PLN - 1; i >= 0; --i) {
-      if (!greedy) ws += (double)block_w(r.M[i], r.S[i], m, s);
-      const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
-      if (mk) am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
-    }
-    ws = wave_sum_d(ws);
-    if (lane == 0) {
-      g.m[j] = m;
-      g.L[j] = greedy ? 0.0 : ln_fast(ws);
-      g.am[j] = am < 0 ? 0 : am;
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    bool rej = false;
-    if (lane < Jd) {
-      const int xj = p.dtok[b * K + lane];
-      if (xj < 0 || xj >= V) {
-        rej = true;
-      } else if (greedy) {
-        rej = xj != g.am[lane];
-      } else {
-        const double pj = exp_fast(((double)p.zcap[b * K + lane] - (double)g.m[lane]) * (1.0 / (double)T) - g.L[lane]);
-        const double q = (double)p.dq[b * K + lane];
-        const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
-        const double u = (double)uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
-        rej = u >= rho * (1.0 + 1e-4) + 1e-30;
-      }
-    }
-    const uint64_t rm = __ballot(rej);
-    if (lane == 0) g.alive = rm == 0ull;
-  }
-  __syncthreads();
-  return g.alive != 0;
-}
-
-// Streaming pass of verification over positions jlo .. jlo + jn - 1, for the
-// sequences that seq_alive keeps (the others' workgroups return at once).
-template <int DT, bool AL>
-__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream_gated(Params p) {
-  __shared__ GateSm g;
-  const int b = (int)((blockIdx.x / p.nchunk) / p.jn);
-  const bool alive = p.NB <= 128 ? seq_alive<2>(p, b, p.jlo, g) : seq_alive<NBL>(p, b, p.jlo, g);
-  if (!alive) return;
-  stream_item<DT, AL, M_VERIFY>(p, blockIdx.x);
-}
-
-// Sampling epilogue item g: row g, or (g >= rows) a long cache-key list.
-template <int DT, bool AL>
-__device__ __forceinline__ void sample_epi_item(const Params& p, int g, ESm& sm) {
-  const bool small = p.NB <= 128;
-  if (g < p.rows) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
-  else small ? epi_keys_p<DT, AL, 2>(p, g - (int)p.rows, sm) : epi_keys_p<DT, AL, NBL>(p, g - (int)p.rows, sm);
-}
-
-// One workgroup per row (per sequence for verification) over the partials.
-template <int DT, bool AL, int MODE>
-__global__ __launch_bounds__(EWG) void k_epi(Params p) {
-  __shared__ ESm sm;
-  const int g = blockIdx.x;
-  // rows of up to 128 blocks (V <= 262144) keep two partials per lane
-  const bool small = p.NB <= 128;
-  if constexpr (MODE == M_SOFTMAX) small ? epi_softmax_p<DT, AL, 2>(p, g) : epi_softmax_p<DT, AL, NBL>(p, g);
-  if constexpr (MODE == M_TOPF) small ? epi_topf_p<DT, AL, 2>(p, g, sm) : epi_topf_p<DT, AL, NBL>(p, g, sm);
-  if constexpr (MODE == M_SAMPLE) sample_epi_item<DT, AL>(p, g, sm);
-}
-
-// Acceptance and residual pass (one workgroup per sequence and chunk).
-template <int DT, bool AL>
-__device__ __forceinline__ void accept_item(const Params& p, int item, ESm& sm) {
-  const int b = item / p.nchunk, chunk = item - b * p.nchunk;
-  if (p.NB <= 128) accept_residual<DT, AL, 2>(p, b, chunk, sm);
-  else accept_residual<DT, AL, NBL>(p, b, chunk, sm);
-}
-
-template <int DT, bool AL>
-__global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_accept(Params p) {
-  __shared__ ESm sm;
-  accept_item<DT, AL>(p, blockIdx.x, sm);
 }
 
 // Wave 0's copy of sequence b's keys and payload, one slot per lane, when
@@ -1447,68 +1080,590 @@ __device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k,
                                             : -1;
 }
 
-// Bonus from the residual for the sequences that need it, then (when asked)
-// the cache lookup of every sequence's (k*, bonus).
-template <int DT, bool AL>
-__device__ __forceinline__ void residual_item(const Params& p, int b, ESm& sm) {
-  const int NB = p.NB;
-  SSD_PHASE(2, b, 0);
-  // the residual sums (used only when the state asks for them), the state,
-  // and the outcome of sequences decided earlier are loaded together
-  // (unconditional loads from clamped addresses: all in flight at once)
-  float R[NBT], Mt[NBT];
-  float2 rv[NBT];
-#pragma unroll
-  for (int k = 0; k < NBT; ++k) rv[k] = p.rpart[(int64_t)b * NB + min((int)threadIdx.x + k * EWG, NB - 1)];
-#pragma unroll
-  for (int k = 0; k < NBT; ++k) {
-    const bool in = (int)threadIdx.x + k * EWG < NB;
-    R[k] = in ? rv[k].x : 0.f;
-    Mt[k] = in ? rv[k].y : -INFINITY;
-  }
-  const SeqState ss = p.state[b];
-  const int ks0 = p.lookup ? p.acc_len[b] : 0, y0 = p.lookup ? p.bonus[b] : 0;
+// ---------------------------------------------------------------------------
+// Verification of one sequence after its streaming pass (one workgroup):
+// statistics of the K + 1 target rows from their partials, the acceptance
+// decisions, the bonus and the cache lookup.
+//
+// The bonus after a rejection at k* is drawn from the residual max(0, p -
+// sigma) of row k* by the same two-level race as everywhere (block by its
+// residual sum R_be, then a token inside the block), but the block race is
+// evaluated lazily: R_be <= P_be, the block's target mass known from the
+// streaming partials, so the block key -log2(u_be) / R_be is bounded below
+// by -log2(u_be) / P_be.  Blocks are evaluated (both rows re-read, R_be
+// summed) smallest bound first, up to LZ_G at a time, until no block left
+// has a bound at or below the best exact key: the winner is then the block
+// the full race over every R_be would pick, and about 1 / (rejection
+// probability) blocks are read instead of two whole rows.  The bound is
+// taken with P_be (1 + 1e-3), far above the rounding of either sum.
+// ---------------------------------------------------------------------------
+constexpr int PM_CAP = 1024;          // per-row block values of the K + 1 rows kept in LDS when (K + 1) NB fits
+constexpr int LZ_G = 2 * ENW;         // blocks per round of the lazy block race (two per wave)
+constexpr float LZ_INFL = 1.001f;     // R_be <= P_be LZ_INFL
+constexpr uint32_t LB_NONE = ~0u;     // no bound: past the row or already evaluated
+constexpr uint32_t LB_INF = 0x7F800000u;  // P_be = 0: evaluated only while no block has residual mass
+constexpr int LZ_NT = 8;              // steps of the selection ladder
+
+struct VSm {
+  uint64_t ru[6][ENW];
+  float pM[PM_CAP];         // row j's block be at j NB + be (or only row k* or K, at be)
+  float pS[PM_CAP];
+  uint32_t lbk[PM_CAP];     // lower bound of row j's block key (the bits of a non-negative float)
+  float nlv[PM_CAP];        // -log2(u) of row j's block draw
+  int tf[TF_CAP];           // the draft top-F lists of the sequence's rows
+  int ckey[64];             // the sequence's cache keys and payload when they fit (CacheRegs)
+  int cpay[64 * KREG];
+  int ks;
+  SeqState ss;
+  float vm[MAX_K1];
+  double vL[MAX_K1];
+  int vfb[MAX_K1];
+  int vam[MAX_K1];
+};
+
+// Block bound of the lazy race: -log2(u) / (W LZ_INFL), LB_INF when W = 0.
+__device__ __forceinline__ uint32_t lazy_bound(float nl, float W) {
+  return W > 0.f ? __float_as_uint(nl * __builtin_amdgcn_rcpf(W * LZ_INFL)) : LB_INF;
+}
+
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
+  const int K = p.K, K1 = K + 1, NB = p.NB, tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int V = (int)p.V;
+  const float T = p.temp[b];
+  const bool greedy = !(T > 0.f);
+  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
+  const double invT = greedy ? 0.0 : 1.0 / (double)T;
+  const int64_t r0 = (int64_t)b * K1;
+  const int64_t rs = p.ld * Dt<DT>::SZ;
+  // rows of up to 128 blocks (two per lane) keep their block values in LDS
+  // when the K + 1 rows fit
+  const bool fit = PLN <= 2 && K1 * NB <= PM_CAP;
+  SSD_PH_DECL;
+  SSD_PH(0);
+  // wave 0, lane j < K: drafted token, sigma_j(x_j), the target logit at x_j
+  // captured by the streaming pass; lane j <= K: the draft row statistics;
+  // thread t < (K+1) F: entry t of the draft top-F lists of all K + 1 rows
+  // (the residual of row k* needs one); wave 0: the cache keys and payload.
+  // All loaded unconditionally from clamped indices (a valid stand-in array
+  // when K = 0 or F = 0: the captured-logit workspace), so that they and the
+  // partials below are in flight together (a load under a branch gets a wait
+  // of its own) and no load waits on k*.
+  const int F = p.F;
+  const bool tf_lds = F > 0 && K1 * F <= TF_CAP;
+  const int tq = min(tid, max(K - 1, 0));
+  const int32_t* dtok = K > 0 ? p.dtok : reinterpret_cast<const int32_t*>(p.zcap);
+  const float* dqp = K > 0 ? p.dq : p.zcap;
+  const int xl = dtok[b * K + tq];
+  const float ql = dqp[b * K + tq], zl = p.zcap[b * K + tq];
+  const ssd_row_stats ds = p.dstats[r0 + min(tid, K)];
+  const int tt = tf_lds ? min(tid, K1 * F - 1) : 0;
+  const int32_t* tfp = tf_lds ? p.dtopf + (r0 + tt / F) * p.ld_dtopf + tt % F : reinterpret_cast<const int32_t*>(p.zcap);
+  const int tfv = *tfp;
   CacheRegs cr;
   cache_prefetch(p, b, cr);
-  // the draft top-F lists of all rows, for the residual's sigma (row k*)
-  const int K1 = p.K + 1, F = p.F;
-  const bool tf_lds = F > 0 && K1 * F <= TF_CAP;
-  if (tf_lds && threadIdx.x < K1 * F)
-    sm.tf[threadIdx.x] = p.dtopf[((int64_t)b * K1 + threadIdx.x / F) * p.ld_dtopf + threadIdx.x % F];
-  if (ss.need) epi_residual<DT, AL>(p, b, ss, R, Mt, tf_lds, sm);
-  if (!p.lookup) return;
-  if (ss.need) {
-    __syncthreads();
-    if (threadIdx.x < 64) cache_lookup_wave(p, b, ss.kstar, sm.bonus, cr);
-  } else if (threadIdx.x < 64) {
-    cache_lookup_wave(p, b, ks0, y0, cr);
+  const int xj = tid < K ? xl : -1;
+  const float qj = tid < K ? ql : 0.f, ztj = tid < K ? zl : 0.f;
+  const float dmax = (tid <= K && !greedy) ? ds.max : 0.f;
+  const double dlse = (tid <= K && !greedy) ? (double)ds.lse : 0.0;
+  // row statistics: wave w merges rows j = w, w + ENW, ..., two rows per pass
+  // with both rows' loads in flight.  When the rows fit in LDS, their (M, S)
+  // stay there with, for rows j < K of T > 0 sequences, the lazy race's
+  // block draws (carried by the partials) and bounds.
+  const bool pre = fit && !greedy;
+  auto merge = [&](const WRow<PLN>& r, int j) {
+    float lm = r.M[0];
+#pragma unroll
+    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+    const float m = wave_max(lm);
+    int fb = -1, am = -1;
+    double wsum = 0.0;
+    float W[PLN];
+#pragma unroll
+    for (int i = PLN - 1; i >= 0; --i) {
+      W[i] = greedy ? 0.f : block_w(r.M[i], r.S[i], m, s);
+      wsum += (double)W[i];
+      const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
+      if (mk) {
+        fb = 64 * i + (int)__builtin_ctzll(mk);
+        am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
+      }
+    }
+    wsum = wave_sum_d(wsum);
+    if (pre) {
+#pragma unroll
+      for (int i = 0; i < PLN; ++i) {
+        const int be = lane + 64 * i;
+        if (be < NB) {
+          sm.pM[j * NB + be] = r.M[i];
+          sm.pS[j * NB + be] = r.S[i];
+          if (j < K) {
+            const float nl = __int_as_float(r.I[i]);  // the block draw, from the streaming pass
+            sm.lbk[j * NB + be] = lazy_bound(nl, W[i]);
+            sm.nlv[j * NB + be] = nl;
+          }
+        }
+      }
+    }
+    if (lane == 0) {
+      sm.vm[j] = m;
+      sm.vL[j] = greedy ? 0.0 : ln_fast(wsum);
+      sm.vfb[j] = fb < 0 ? 0 : fb;                  // (a NaN row matches no block)
+      sm.vam[j] = greedy ? (am < 0 ? 0 : am) : -1;  // greedy rows carry the block argmax in their partial
+    }
+  };
+  float uacc = 0.f;
+  for (int j0 = wave; j0 < K1; j0 += 2 * ENW) {
+    const int j1 = j0 + ENW;
+    WRow<PLN> ra, rb;
+    load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
+    load_wrow<PLN>(p.part + (r0 + min(j1, K)) * NB, NB, rb);
+    // wave 0, lane j: the acceptance draw u_j, computed while the partials load
+    if (wave == 0 && j0 == 0 && !greedy)
+      uacc = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
+    merge(ra, j0);
+    if (j1 < K1) merge(rb, j1);
   }
-  SSD_PHASE(2, b, 5);  // cache lookup
+  if (tf_lds && tid < K1 * F) sm.tf[tid] = tfv;
+  // the cache keys and payload wait in LDS (registers are short later on)
+  if (cr.ok && tid < 64) {
+    sm.ckey[lane] = cr.key;
+#pragma unroll
+    for (int i = 0; i < KREG; ++i) sm.cpay[lane * KREG + i] = cr.pay[i];
+  }
+  lds_sync();
+  SSD_PH(1);  // prologue loads and the K+1 rows' statistics
+  // argmax of the T > 0 rows is only needed for the optional statistics
+  if (!greedy && p.stats) {
+    for (int j = wave; j < K1; j += ENW) {
+      const int am = wave_first_eq<DT, AL>(p.x + (r0 + j) * rs, V, sm.vfb[j], sm.vm[j]);
+      if (lane == 0) sm.vam[j] = am;
+    }
+    lds_sync();
+  }
+  // acceptance decisions (wave 0, lane j < K) and p_j(x_j) for every position
+  double pj = 0.0;
+  if (wave == 0) {
+    bool acc = false;
+    if (lane < K && xj >= 0 && xj < V) {
+      if (greedy) {
+        acc = (xj == sm.vam[lane]);
+        pj = acc ? 1.0 : 0.0;
+      } else {
+        pj = exp_fast(((double)ztj - (double)sm.vm[lane]) * invT - sm.vL[lane]);
+        const double q = (double)qj;
+        const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
+        acc = (double)uacc < rho;
+      }
+    }
+    const uint64_t rej = __ballot(lane < K && !acc);
+    const int ks = rej ? (int)__builtin_ctzll(rej) : K;
+    SeqState ss{};
+    ss.kstar = ks;
+    if (!greedy && ks < K) {
+      // the residual's constants (target and draft row k*)
+      const float mt = sm.vm[ks];
+      const float md = rl_f(dmax, ks);
+      const double Ld = rl_d(dlse, ks), Lt = sm.vL[ks];
+      ss.need = 1;
+      ss.s = s;
+      ss.m_t = mt;
+      ss.o_t = -mt * s;
+      ss.o_d = -md * s;
+      const double et = (double)ss.o_t + (double)mt * (double)s;
+      const double ed = (double)ss.o_d + (double)md * (double)s;
+      ss.invT = invT;
+      ss.D0 = ((double)mt - (double)md) * invT + Lt - Ld;
+      ss.lnC = ln_fast((double)p.C);
+      ss.kf = (float)exp_fast((et - ed) * LN2 + (Lt - Ld));
+    }
+    if (lane == 0) {
+      sm.ks = ks;
+      sm.ss = ss;
+    }
+  }
+  lds_sync();
+  SSD_PH(2);  // acceptance decisions
+  const int ks = sm.ks;
+  const float pjf = (float)pj;
+  int y = greedy ? sm.vam[ks] : 0;  // the bonus
+  if (!greedy) {
+    // row k*'s partials (row K when every token is accepted): kept by the
+    // merge, or read again now
+    int pb = ks * NB;
+    if (!fit) {
+      for (int be = tid; be < NB; be += EWG) {
+        const float4 v = p.part[(r0 + ks) * NB + be];
+        sm.pM[be] = v.x;
+        sm.pS[be] = v.y;
+        sm.nlv[be] = v.z;
+      }
+      lds_sync();
+      pb = 0;
+    }
+    int x;
+    if (ks == K) {
+      // all K accepted: bonus ~ p_K
+      const float m = sm.vm[K];
+      int beta = block_stage(NB, p.seed, b, K, ST_BONUS_BLOCK, sm.ru[0], [&](int be, int) -> float {
+        return block_w(sm.pM[pb + be], sm.pS[pb + be], m, s);
+      });
+      if (beta < 0) beta = 0;
+      const unsigned char* rp = p.x + (r0 + K) * rs;
+      const int x0 = beta * BLK + TPT * tid;
+      Run<DT, AL> run;
+      run_issue<DT, AL>(rp, V, x0, run);
+      const RaceWords rw = race_words(x0, p.seed, b, K, ST_BONUS_TOKEN);  // while the block loads
+      __builtin_amdgcn_sched_barrier(0);
+      float z[TPT];
+      run_finish<DT, AL>(V, x0, run, z);
+      const float Mb = sm.pM[pb + beta];
+      x = token_race(x0, V, rw, sm.ru[1], [&](int e) -> float {
+        return z[e] > -INFINITY ? (Mb - z[e]) * s : INFINITY;
+      });
+      SSD_PH(3);
+    } else {
+      // lazy block race over the residual of row k*
+      const SeqState ss = sm.ss;
+      const int64_t row = r0 + ks;
+      const unsigned char* rt = p.x + row * rs;
+      const unsigned char* rd = p.xd + row * rs;
+      const int32_t* tfl = F <= 0 ? nullptr : tf_lds ? sm.tf + ks * F : p.dtopf + row * p.ld_dtopf;
+      const float ot = ss.o_t, od = ss.o_d, nk = -ss.kf, nkc = nk * p.C, mt = ss.m_t;
+      // every wave holds every block's bound (block be = lane + 64 i in slot i)
+      uint32_t lb[PLN];
+      float nl[PLN];
+#pragma unroll
+      for (int i = 0; i < PLN; ++i) {
+        const int be = lane + 64 * i;
+        const bool in = be < NB;
+        if (fit) {
+          lb[i] = in ? sm.lbk[pb + be] : LB_NONE;
+          nl[i] = in ? sm.nlv[pb + be] : 0.f;
+        } else {
+          const float W = in ? block_w(sm.pM[pb + be], sm.pS[pb + be], mt, s) : 0.f;
+          nl[i] = in ? sm.nlv[pb + be] : 0.f;
+          lb[i] = in ? lazy_bound(nl[i], W) : LB_NONE;
+        }
+      }
+      uint64_t best = NO_KEY;
+      int nev = 0;
+      for (int round = 0;; ++round) {
+        // the candidates: bounds at or below the best key so far.  A round
+        // takes those up to m c_t (m: the smallest; c_t: the ladder's largest
+        // step that keeps them within LZ_G), or the first LZ_G of the ties at
+        // m; the same choice in every wave.
+        const uint32_t lim = (uint32_t)(best >> 32);
+        uint32_t mn = lb[0];
+#pragma unroll
+        for (int i = 1; i < PLN; ++i) mn = min(mn, lb[i]);
+        mn = wave_min_u32(mn);
+        if (mn == LB_NONE || mn > lim) break;
+        constexpr float ladder[LZ_NT] = {1.f, 1.5f, 2.f, 3.f, 4.f, 8.f, 16.f, 64.f};
+        const float mf = __uint_as_float(mn);
+        uint32_t thr = mn;
+#pragma unroll
+        for (int t = 1; t < LZ_NT; ++t) {
+          const uint32_t tb = min(__float_as_uint(mf * ladder[t]), lim);
+          int cnt = 0;
+#pragma unroll
+          for (int i = 0; i < PLN; ++i) cnt += __popcll(__ballot(lb[i] <= tb));
+          thr = cnt <= LZ_G ? tb : thr;
+        }
+        // the chosen blocks (the first LZ_G at or below the threshold, in
+        // increasing index), two per wave; every wave marks all of them
+        // evaluated
+        int sel0 = -1, sel1 = -1, nsel = 0;
+#pragma unroll
+        for (int i = 0; i < PLN; ++i) {
+          const uint64_t m0 = __ballot(lb[i] <= thr);
+          uint64_t mk = m0;
+          while (mk && nsel < LZ_G) {
+            const int be = 64 * i + (int)__builtin_ctzll(mk);
+            mk &= mk - 1ull;
+            sel0 = nsel == wave ? be : sel0;
+            sel1 = nsel == wave + ENW ? be : sel1;
+            ++nsel;
+          }
+          lb[i] = ((m0 ^ mk) >> lane) & 1ull ? LB_NONE : lb[i];
+        }
+        float n0 = 0.f, n1 = 0.f;
+        if (sel0 >= 0) n0 = slot_at<PLN>(nl, sel0);
+        if (sel1 >= 0) n1 = slot_at<PLN>(nl, sel1);
+        nev += nsel;
+        uint64_t wb = NO_KEY;
+        if (sel0 >= 0) {
+          const int c1 = sel1 >= 0 ? sel1 : sel0;
+          RawBlock<DT, AL> ut0, ud0, ut1, ud1;
+          // ordinary loads: the chosen block is read again by the token stage
+          if ((max(sel0, c1) + 1) * BLK <= V) {
+            load_raw<DT, AL, true, false>(rt, V, sel0, lane, ut0);
+            load_raw<DT, AL, true, false>(rd, V, sel0, lane, ud0);
+            load_raw<DT, AL, true, false>(rt, V, c1, lane, ut1);
+            load_raw<DT, AL, true, false>(rd, V, c1, lane, ud1);
+          } else {
+            load_raw<DT, AL, false>(rt, V, sel0, lane, ut0);
+            load_raw<DT, AL, false>(rd, V, sel0, lane, ud0);
+            load_raw<DT, AL, false>(rt, V, c1, lane, ut1);
+            load_raw<DT, AL, false>(rd, V, c1, lane, ud1);
+          }
+          const float R0 = block_residual<DT, AL>(ut0, ud0, sel0, V, s, ot, od, nk, nkc, F, tfl);
+          if (R0 > 0.f) wb = race_key(n0 * __builtin_amdgcn_rcpf(R0), sel0);
+          if (sel1 >= 0) {
+            const float R1 = block_residual<DT, AL>(ut1, ud1, sel1, V, s, ot, od, nk, nkc, F, tfl);
+            if (R1 > 0.f) wb = umin64(wb, race_key(n1 * __builtin_amdgcn_rcpf(R1), sel1));
+          }
+        }
+        // (two alternating slots: a wave rewrites one only after the next
+        // barrier, which every wave reaches after reading it)
+        uint64_t* slot = sm.ru[2 + (round & 1)];
+        if (lane == 0) slot[wave] = wb;
+        lds_sync();
+#pragma unroll
+        for (int w = 0; w < ENW; ++w) best = umin64(best, slot[w]);
+      }
+      SSD_PH(3);  // lazy block race
+      SSD_PH_SET(7, nev);
+      (void)nev;
+      const bool any = best != NO_KEY;
+      int beta = (int)(uint32_t)best;
+      if (!any) {
+        // no residual mass (every block evaluated): p_k*
+        beta = block_stage(NB, p.seed, b, ks, ST_BONUS_BLOCK, sm.ru[0], [&](int be, int) -> float {
+          return block_w(sm.pM[pb + be], sm.pS[pb + be], mt, s);
+        });
+        if (beta < 0) beta = 0;
+      }
+      x = residual_token<DT, AL>(p, b, ss, beta, sm.pM[pb + beta], any, tfl, sm.ru[1], sm.ru[4]);
+    }
+    y = (x >= 0 && x < V) ? x : 0;
+  }
+  SSD_PH(4);  // bonus token
+  if (p.lookup && tid < 64) {
+    CacheRegs c2;
+    c2.ok = cr.ok;
+    c2.key = cr.ok ? sm.ckey[lane] : 0;
+#pragma unroll
+    for (int i = 0; i < KREG; ++i) c2.pay[i] = cr.ok ? sm.cpay[lane * KREG + i] : -1;
+    cache_lookup_wave(p, b, ks, y, c2);
+  }
+  SSD_PH(5);  // cache lookup
+  // the per-sequence outputs, stored last: a barrier, or a wait for an older
+  // load, after a store waits for the store too (one counter covers both)
+  if (wave == 0) {
+    // (early exit: the rows past k* may not have been read)
+    if (lane < K) p.p_out[b * K + lane] = (p.early && lane > ks) ? __builtin_nanf("") : pjf;
+    if (lane == 0) {
+      p.acc_len[b] = ks;
+      p.bonus[b] = y;
+    }
+  }
+  if (p.stats && tid < K1) {
+    ssd_row_stats st;
+    st.lse = sm.vL[tid];
+    st.max = sm.vm[tid];
+    st.argmax = sm.vam[tid];
+    p.stats[r0 + tid] = st;
+  }
+  SSD_PH_FLUSH(1, b);
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+// (f32 and unaligned rows need more registers per element: fewer waves)
+template <int DT, bool AL, int MODE>
+__device__ __forceinline__ void stream_item(const Params& p, int item) {
+  const int64_t it = item / p.nchunk;
+  const int chunk = item - (int)(it * p.nchunk);
+  const int64_t row = p.jn > 0 ? (it / p.jn) * (p.K + 1) + p.jlo + (it % p.jn) : it;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K1 = p.K + 1;
+  const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
+  const int V = (int)p.V, NB = p.NB;
+  const int b0 = chunk * CH + wave, b1 = b0 + NWAVE;
+  // the logit loads are issued first; the temperature (and the drafted
+  // token) are fetched behind them
+  RawBlock<DT, AL> r0, r1;
+  const bool full = (chunk + 1) * CH * BLK <= V;
+  // verification: the first p.keep target rows of a sequence, the likeliest
+  // rows of the first rejection, are read with ordinary loads so that the
+  // residual pass's re-read of row k* may find them in the Infinity Cache
+  const bool keep = MODE == M_VERIFY && (int)(row % K1) < p.keep;
+  if (full && keep) {
+    load_raw<DT, AL, true, false>(rp, V, b0, lane, r0);
+    load_raw<DT, AL, true, false>(rp, V, b1, lane, r1);
+  } else if (full) {
+    // every block of this chunk is full: all loads in flight together
+    load_raw<DT, AL, true>(rp, V, b0, lane, r0);
+    load_raw<DT, AL, true>(rp, V, b1, lane, r1);
+  } else {
+    // the chunk holding the ragged end of the row
+    load_raw<DT, AL, false>(rp, V, min(b0, NB - 1), lane, r0);
+    load_raw<DT, AL, false>(rp, V, min(b1, NB - 1), lane, r1);
+  }
+  float T = 0.f;
+  if constexpr (MODE == M_SOFTMAX) T = p.temp[row];
+  if constexpr (MODE == M_SAMPLE || MODE == M_VERIFY) T = p.temp[row / K1];
+  const double sd = LOG2E / (double)T;
+  const float s = (T > 0.f) ? (float)sd : 0.f;
+  int xj = -1;  // verification: drafted token of this target row (j < K)
+  if constexpr (MODE == M_VERIFY) {
+    const int j = (int)(row % K1);
+    if (j < p.K && p.dtok) xj = p.dtok[(row / K1) * p.K + j];
+  }
+  float v[32];
+  decode_raw<DT, AL>(r0, v);
+  float4 P0 = block_partial<DT, MODE>(v, s, min(b0, NB - 1), lane);
+  decode_raw<DT, AL>(r1, v);
+  float4 P1 = block_partial<DT, MODE>(v, s, min(b1, NB - 1), lane);
+  if constexpr (MODE == M_VERIFY) {
+    // T > 0 rows leave I unused: it carries -log2(u) of the block's draw for
+    // a bonus from this row, u(idx = block, b, j, bonus-block stream), which
+    // the verification's lazy block race reads with the partials (the
+    // counters are uniform in the workgroup: scalar arithmetic)
+    if (s > 0.f) {
+      const uint32_t bq = (uint32_t)(row / K1), jq = (uint32_t)(row % K1);
+      P0.z = neg_log2_u(draw1(p.seed, (uint32_t)b0, bq, jq, ST_BONUS_BLOCK));
+      P1.z = neg_log2_u(draw1(p.seed, (uint32_t)b1, bq, jq, ST_BONUS_BLOCK));
+    }
+  }
+  if (lane == 0 && b0 < NB) p.part[row * NB + b0] = P0;
+  if (lane == 0 && b1 < NB) p.part[row * NB + b1] = P1;
+  if constexpr (MODE == M_VERIFY) {
+    // the workgroup whose chunk holds x_j hands its target logit to the epilogue
+    if (xj >= 0 && xj < V && xj / (CH * BLK) == chunk && threadIdx.x == 0)
+      p.zcap[(row / K1) * p.K + (row % K1)] = load_elem<DT>(rp, xj);
+  }
+}
+
+template <int DT, bool AL, int MODE>
+__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream(Params p) {
+  stream_item<DT, AL, MODE>(p, blockIdx.x);
+}
+
+// Early-exit verification.  A sequence's verification never reads target
+// rows past its first rejection, so once positions 0 .. J-1 have been
+// streamed, the rows from J on are needed only by sequences without a
+// rejection below J.  seq_alive judges that from the partials of rows < J
+// (written by the previous launch) conservatively: false only when some
+// position j < J is rejected with a clear margin (T > 0: u_j >= rho_j (1 +
+// 1e-4); greedy: x_j is not the row's argmax; or x_j outside [0, V)), so a
+// sequence that the acceptance pass may find unrejected below J is never
+// skipped.  Every thread calls; the result is uniform.
+struct GateSm {
+  float m[MAX_K1];
+  double L[MAX_K1];
+  int am[MAX_K1];
+  int alive;
+};
+template <int PLN>
+__device__ __forceinline__ bool seq_alive(const Params& p, int b, int J, GateSm& g) {
+  const int K = p.K, K1 = K + 1, NB = p.NB, V = (int)p.V;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float T = p.temp[b];
+  const bool greedy = !(T > 0.f);
+  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
+  const int Jd = min(J, K);  // positions with a decision
+  for (int j = wave; j < Jd; j += NWAVE) {
+    WRow<PLN> r;
+    load_wrow<PLN>(p.part + ((int64_t)b * K1 + j) * NB, NB, r);
+    float lm = r.M[0];
+#pragma unroll
+    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+    const float m = wave_max(lm);
+    double ws = 0.0;
+    int am = -1;
+#pragma unroll
+    for (int i = PLN - 1; i >= 0; --i) {
+      if (!greedy) ws += (double)block_w(r.M[i], r.S[i], m, s);
+      const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
+      if (mk) am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
+    }
+    ws = wave_sum_d(ws);
+    if (lane == 0) {
+      g.m[j] = m;
+      g.L[j] = greedy ? 0.0 : ln_fast(ws);
+      g.am[j] = am < 0 ? 0 : am;
+    }
+  }
+  lds_sync();
+  if (wave == 0) {
+    bool rej = false;
+    if (lane < Jd) {
+      const int xj = p.dtok[b * K + lane];
+      if (xj < 0 || xj >= V) {
+        rej = true;
+      } else if (greedy) {
+        rej = xj != g.am[lane];
+      } else {
+        const double pj = exp_fast(((double)p.zcap[b * K + lane] - (double)g.m[lane]) * (1.0 / (double)T) - g.L[lane]);
+        const double q = (double)p.dq[b * K + lane];
+        const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
+        const double u = (double)uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
+        rej = u >= rho * (1.0 + 1e-4) + 1e-30;
+      }
+    }
+    const uint64_t rm = __ballot(rej);
+    if (lane == 0) g.alive = rm == 0ull;
+  }
+  lds_sync();
+  return g.alive != 0;
+}
+
+// Streaming pass of verification over positions jlo .. jlo + jn - 1, for the
+// sequences that seq_alive keeps (the others' workgroups return at once).
+template <int DT, bool AL>
+__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream_gated(Params p) {
+  __shared__ GateSm g;
+  const int b = (int)((blockIdx.x / p.nchunk) / p.jn);
+  const bool alive = p.NB <= 128 ? seq_alive<2>(p, b, p.jlo, g) : seq_alive<NBL>(p, b, p.jlo, g);
+  if (!alive) return;
+  stream_item<DT, AL, M_VERIFY>(p, blockIdx.x);
+}
+
+// Sampling epilogue item g: row g, or (g >= rows) a long cache-key list.
+template <int DT, bool AL>
+__device__ __forceinline__ void sample_epi_item(const Params& p, int g, ESm& sm) {
+  const bool small = p.NB <= 128;
+  if (g < p.rows) small ? epi_sample_p<DT, AL, 2>(p, g, sm) : epi_sample_p<DT, AL, NBL>(p, g, sm);
+  else small ? epi_keys_p<DT, AL, 2>(p, g - (int)p.rows, sm) : epi_keys_p<DT, AL, NBL>(p, g - (int)p.rows, sm);
+}
+
+// One workgroup per row (per sequence for verification) over the partials.
+template <int DT, bool AL, int MODE>
+__global__ __launch_bounds__(EWG) void k_epi(Params p) {
+  __shared__ ESm sm;
+  const int g = blockIdx.x;
+  // rows of up to 128 blocks (V <= 262144) keep two partials per lane
+  const bool small = p.NB <= 128;
+  if constexpr (MODE == M_SOFTMAX) small ? epi_softmax_p<DT, AL, 2>(p, g) : epi_softmax_p<DT, AL, NBL>(p, g);
+  if constexpr (MODE == M_TOPF) small ? epi_topf_p<DT, AL, 2>(p, g, sm) : epi_topf_p<DT, AL, NBL>(p, g, sm);
+  if constexpr (MODE == M_SAMPLE) sample_epi_item<DT, AL>(p, g, sm);
+}
+
+// Verification after the streaming pass: one workgroup per sequence.
+template <int DT, bool AL>
+__device__ __forceinline__ void verify_item(const Params& p, int b, VSm& sm) {
+  if (p.NB <= 128) verify_seq<DT, AL, 2>(p, b, sm);
+  else verify_seq<DT, AL, NBL>(p, b, sm);
 }
 
 template <int DT, bool AL>
-__global__ __launch_bounds__(EWG) void k_residual_epi(Params p) {
-  __shared__ ESm sm;
-  residual_item<DT, AL>(p, blockIdx.x, sm);
+__global__ __launch_bounds__(EWG) void k_verify_seq(Params p) {
+  __shared__ VSm sm;
+  verify_item<DT, AL>(p, blockIdx.x, sm);
 }
 
-// One round of the pipeline in two launches that each pair a latency-bound
-// kernel of verification (round i) with a kernel of sampling (round i + 1),
-// which does not depend on it: workgroups below nv take the verification
-// role.  (1) acceptance and residual pass beside sampling's streaming pass;
-// (2) bonus and cache lookup beside sampling's epilogue.
+// One round of the pipeline: the verification of round i (one workgroup per
+// sequence, below nv) beside the streaming pass of round i + 1's sampling,
+// which does not depend on it.
 template <int DT, bool AL>
 __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_round_mid(Params pv, Params ps, int nv) {
-  __shared__ ESm sm;
-  if ((int)blockIdx.x < nv) accept_item<DT, AL>(pv, blockIdx.x, sm);
+  __shared__ VSm sm;
+  if ((int)blockIdx.x < nv) verify_item<DT, AL>(pv, blockIdx.x, sm);
   else stream_item<DT, AL, M_SAMPLE>(ps, (int)blockIdx.x - nv);
-}
-
-template <int DT, bool AL>
-__global__ __launch_bounds__(EWG) void k_round_tail(Params pv, Params ps, int nv) {
-  __shared__ ESm sm;
-  if ((int)blockIdx.x < nv) residual_item<DT, AL>(pv, blockIdx.x, sm);
-  else sample_epi_item<DT, AL>(ps, (int)blockIdx.x - nv, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1598,7 +1753,7 @@ __device__ __forceinline__ void tree_item(const Params& p, const TreeArgs& ta, i
       }
     }
   }
-  __syncthreads();
+  lds_sync();
   int n = 0, depth = 0, cur = 0;
   double c = 0.0, Nr = 1.0;  // residual max(0, p - c sigma) / Nr at node n
   bool res = false;          // the bonus comes from a residual with mass
@@ -1650,7 +1805,7 @@ __device__ __forceinline__ void tree_item(const Params& p, const TreeArgs& ta, i
       const unsigned char* rd = p.xd + row * rs;
       const int32_t* tfrow = F > 0 ? p.dtopf + row * p.ld_dtopf : nullptr;
       if (tid < F) sm.tf[tid] = tfrow[tid];
-      __syncthreads();
+      lds_sync();
       double wacc = 0.0;
       for (int base = 0; base < NB; base += CH_R) {
         const int be0 = base + wave, be1 = be0 + ENW;
@@ -1673,43 +1828,13 @@ __device__ __forceinline__ void tree_item(const Params& p, const TreeArgs& ta, i
           if (be >= NB) break;
           const RawBlock<DT, AL>& ut = h ? ut1 : ut0;
           const RawBlock<DT, AL>& ud = h ? ud1 : ud0;
-          float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-          for (int k = 0; k < 32; k += 2) {
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k), s, ot));
-            const float e2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k), s, od));
-            const float f1 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ut, k + 1), s, ot));
-            const float f2 = __builtin_amdgcn_exp2f(fmaf(raw_elem<DT, AL>(ud, k + 1), s, od));
-            a0 += fmaxf(fmaf(nk, e2, e1), 0.f);
-            a1 += fmaxf(fmaf(nk, f2, f1), 0.f);
-          }
-          float R = wave_sum(a0 + a1);
-          // members of the draft's top-F set carry the factor C
-          for (int f = 0; f < F; ++f) {
-            const int xs = sm.tf[f];
-            if (xs >= 0 && xs < V && xs / BLK == be) {
-              constexpr int VW = Dt<DT>::VW;
-              const int off = xs - be * BLK, gi = off / VW, kk = (gi >> 6) * VW + off % VW;
-              float zt = raw_elem<DT, AL>(ut, 0), zd = raw_elem<DT, AL>(ud, 0);
-#pragma unroll
-              for (int k = 1; k < 32; ++k) {
-                zt = k == kk ? raw_elem<DT, AL>(ut, k) : zt;
-                zd = k == kk ? raw_elem<DT, AL>(ud, k) : zd;
-              }
-              zt = rl_f(zt, gi & 63);
-              zd = rl_f(zd, gi & 63);
-              const float e1 = __builtin_amdgcn_exp2f(fmaf(zt, s, ot));
-              const float e2 = __builtin_amdgcn_exp2f(fmaf(zd, s, od));
-              R += fmaxf(fmaf(nkc, e2, e1), 0.f) - fmaxf(fmaf(nk, e2, e1), 0.f);
-            }
-          }
-          R = fmaxf(R, 0.f);
+          const float R = block_residual<DT, AL>(ut, ud, be, V, s, ot, od, nk, nkc, F, sm.tf);
           if (lane == 0) ts.R[nxt][be] = R;
           wacc += (double)R;
         }
       }
       if (lane == 0) ts.rsum[wave] = wacc;
-      __syncthreads();
+      lds_sync();
       double tot = 0.0;
 #pragma unroll
       for (int w = 0; w < ENW; ++w) tot += ts.rsum[w];
@@ -1721,7 +1846,7 @@ __device__ __forceinline__ void tree_item(const Params& p, const TreeArgs& ta, i
         cur = nxt;
         res = true;
       }
-      __syncthreads();  // (the next pass rewrites the other buffer and the top-F list)
+      lds_sync();  // (the next pass rewrites the other buffer and the top-F list)
     }
     if (next < 0) break;
     n = next;
@@ -1753,7 +1878,7 @@ __device__ __forceinline__ void tree_item(const Params& p, const TreeArgs& ta, i
     Mt[k] = in ? tp[min(be, NB - 1)].x : -INFINITY;
     R[k] = (in && res) ? ts.R[cur][be] : 0.f;
   }
-  epi_residual<DT, AL>(p, b, ss, R, Mt, false, sm);
+  epi_residual<DT, AL>(p, b, ss, R, Mt, sm);
 }
 
 template <int DT, bool AL>
@@ -1810,7 +1935,7 @@ __global__ __launch_bounds__(WG) void k_lookup(const int32_t* keys, const int32_
   const bool live = b < B;
   const int k = live ? acc[b] : -1, y = live ? bonus[b] : 0;
   const int key0 = (live && lane < Bgt) ? keys[(int64_t)b * Bgt + lane] : 0;
-  __syncthreads();
+  lds_sync();
   if (!live) return;
   int found = -1;
   if (k >= 0 && k <= K) {
@@ -1843,7 +1968,7 @@ __global__ __launch_bounds__(WG) void k_cache_keys(const int32_t* topf, int ldf,
                                                    int Bgt, int32_t* keys) {
   __shared__ int so[MAX_K1 + 1];
   if ((int)threadIdx.x <= K + 1) so[threadIdx.x] = off[threadIdx.x];
-  __syncthreads();
+  lds_sync();
   const int64_t t = (int64_t)blockIdx.x * WG + threadIdx.x;
   if (t >= (int64_t)B * Bgt) return;
   const int b = (int)(t / Bgt), sl = (int)(t - (int64_t)b * Bgt);

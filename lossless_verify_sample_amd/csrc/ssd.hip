@@ -33,12 +33,11 @@ int64_t nblocks(int64_t V) { return (V + BLK - 1) / BLK; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-  size_t part, state, rpart, zcap, total;
+  size_t part, zcap, total;
 };
 
 // Workspace regions (256-byte aligned): block partials of every streamed row;
-// for verification the per-sequence hand-over state, residual block sums and
-// the target logits at the drafted tokens.  Every region is written before it is read
+// for verification the target logits at the drafted tokens.  Every region is written before it is read
 // within a call, so the workspace needs no initialisation.
 bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   if (n < 1 || V < 1 || V > SSD_MAX_V) return false;
@@ -50,12 +49,10 @@ bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   const int64_t NB = nblocks(V);
   const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY || op == SSD_OP_VERIFY_TREE) ? n * (K + 1) : n;
   L->part = 0;
-  L->state = L->rpart = L->zcap = 0;
+  L->zcap = 0;
   size_t end = al256((size_t)(rows * NB) * sizeof(float4));
   if (op == SSD_OP_VERIFY) {
-    L->state = end;
-    L->rpart = L->state + al256((size_t)n * sizeof(SeqState));
-    L->zcap = L->rpart + al256((size_t)(n * NB) * sizeof(float2));
+    L->zcap = end;
     end = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
   }
   L->total = end;
@@ -100,8 +97,7 @@ SSD_LAUNCHER(LVerifyGated, (k_stream_gated<DT, AL>))
 SSD_LAUNCHER_E(LSoftmaxEpi, (k_epi<DT, AL, M_SOFTMAX>))
 SSD_LAUNCHER_E(LTopfEpi, (k_epi<DT, AL, M_TOPF>))
 SSD_LAUNCHER_E(LSampleEpi, (k_epi<DT, AL, M_SAMPLE>))
-SSD_LAUNCHER_E(LAccept, (k_accept<DT, AL>))
-SSD_LAUNCHER_E(LResidualEpi, (k_residual_epi<DT, AL>))
+SSD_LAUNCHER_E(LVerifySeq, (k_verify_seq<DT, AL>))
 SSD_LAUNCHER(LProbs, (k_probs<DT, AL>))
 
 template <int DT, bool AL>
@@ -131,7 +127,6 @@ struct LRoundMidT {
     return hipGetLastError();
   }
 };
-SSD_LAUNCHER2(LRoundTail, (k_round_tail<DT, AL>))
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
@@ -140,8 +135,6 @@ bool ws_ok(const void* ws, size_t bytes, const Layout& L) {
 }
 
 const int64_t kMaxGrid = 0x7fffffff;
-constexpr int RACC_ROUND = 4;  // residual blocks per workgroup in ssd_round, in units of CH_R
-constexpr int64_t kResidualWgs = 2048;  // fewest residual workgroups of a standalone verification
 // Target rows read with ordinary loads (positions 0 and 1, the likeliest of
 // the first rejection, whose re-read by the residual pass may then hit the
 // Infinity Cache), while those rows of all sequences fit in this many bytes:
@@ -200,9 +193,7 @@ struct Plan {
   int dt = 0;
   bool al = false;
   int64_t g_stream = 0;  // streaming pass
-  int64_t g_accept = 0;  // verification: acceptance and residual pass
-  int nch_accept = 0;
-  int64_t g_tail = 0;    // sampling epilogue / verification bonus kernel
+  int64_t g_tail = 0;    // sampling epilogue / verification after the streaming pass
 };
 
 ssd_status plan_sample(const ssd_sample_args& a, Plan& q) {
@@ -292,14 +283,8 @@ ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
   if (!layout(SSD_OP_VERIFY, B, K, V, &L)) return SSD_ERR_INVALID_ARG;
   if (!ws_ok(a.workspace, a.ws_bytes, L)) return SSD_ERR_WORKSPACE;
   const int64_t rows = (int64_t)B * (K + 1);
-  // residual workgroups of CH_R blocks, or 2 or 4 times that while at least
-  // kResidualWgs of them remain (measured: longer ones merge the partials
-  // fewer times at large batches; shorter ones spread small batches wider)
   const int64_t NB = nblocks(V), nch = cdiv(NB, CH);
-  int racc = CH_R;
-  while (racc < 4 * CH_R && (int64_t)B * cdiv(NB, 2 * racc) >= kResidualWgs) racc *= 2;
-  const int64_t nchr = cdiv(NB, racc);
-  if (rows * nch > kMaxGrid || (int64_t)B * nchr > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  if (rows * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
   p.x = (const unsigned char*)a.target_logits;
   p.xd = (const unsigned char*)a.draft_logits;
   p.V = V; p.ld = ld; p.rows = rows; p.NB = (int)NB; p.nchunk = (int)nch;
@@ -308,8 +293,6 @@ ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
   p.F = F; p.C = C; p.seed = a.seed;
   char* ws = (char*)a.workspace;
   p.part = (float4*)(ws + L.part);
-  p.state = (SeqState*)(ws + L.state);
-  p.rpart = (float2*)(ws + L.rpart);
   p.stats = a.out_target_stats;
   p.dtok = a.draft_tokens;
   p.dq = a.draft_q;
@@ -323,9 +306,6 @@ ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
   q.dt = a.dt;
   q.al = aligned16(a.target_logits, ld, V, a.dt) && aligned16(a.draft_logits, ld, V, a.dt);
   q.g_stream = rows * nch;
-  q.g_accept = (int64_t)B * nchr;
-  q.nch_accept = (int)nchr;
-  p.racc = racc;
   p.keep = (int64_t)B * kKeepRows * V * dt_size(a.dt) <= kKeepBytes ? kKeepRows : 0;
   q.g_tail = B;
   return SSD_OK;
@@ -336,9 +316,7 @@ hipError_t launch_verify(const Plan& q, hipStream_t st) {
   hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
     return dispatch<LVerify>(q.dt, q.al, q.g_stream, p, st, e0, e1);
   });
-  p.nchunk = q.nch_accept;
-  if (e == hipSuccess) e = dispatch<LAccept>(q.dt, q.al, q.g_accept, p, st);
-  if (e == hipSuccess) e = dispatch<LResidualEpi>(q.dt, q.al, q.g_tail, p, st);
+  if (e == hipSuccess) e = dispatch<LVerifySeq>(q.dt, q.al, q.g_tail, p, st);
   return e;
 }
 
@@ -354,6 +332,7 @@ ssd_status plan_round(const ssd_verify_args* v, const ssd_sample_args* s, Plan& 
     if (e != SSD_OK) return e;
   }
   if (v && s && (v->workspace == s->workspace)) return SSD_ERR_WORKSPACE;
+  if (v && s && qv.g_tail + qs.g_stream > kMaxGrid) return SSD_ERR_UNSUPPORTED;
   if (v && s) {
     // round i+1's sampling must not write what round i's verification reads
     const void* w[] = {s->out_tokens, s->out_q, s->out_stats, s->out_topf_idx};
@@ -379,25 +358,20 @@ ssd_status launch_round(const Plan* pqv, const Plan* pqs, hipStream_t st) {
     if (e == hipSuccess) e = launch_sample(qs, st);
     return hip_status(e);
   }
-  // verification's streaming pass; then its acceptance and residual pass
-  // beside sampling's streaming pass; then its bonus (and lookup) beside
-  // sampling's epilogue
+  // verification's streaming pass; then the verification of each sequence
+  // beside sampling's streaming pass; then sampling's epilogue
   Params pv = qv.p;
   hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
     return dispatch<LVerify>(qv.dt, qv.al, qv.g_stream, pv, st, e0, e1);
   });
-  // fewer, longer residual workgroups: they share the GPU with the
-  // streaming pass, whose progress sets the launch's duration
-  pv.racc = CH_R * RACC_ROUND;
-  pv.nchunk = (int)cdiv(pv.NB, pv.racc);
-  const int64_t g_acc = (int64_t)pv.B * pv.nchunk;
+  const int64_t nv = qv.g_tail;
   if (e == hipSuccess) {
     e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
-      return e0 ? dispatch<LRoundMidT>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st, e0, e1)
-                : dispatch<LRoundMid>(qv.dt, qv.al, g_acc + qs.g_stream, pv, qs.p, (int)g_acc, st);
+      return e0 ? dispatch<LRoundMidT>(qv.dt, qv.al, nv + qs.g_stream, pv, qs.p, (int)nv, st, e0, e1)
+                : dispatch<LRoundMid>(qv.dt, qv.al, nv + qs.g_stream, pv, qs.p, (int)nv, st);
     });
   }
-  if (e == hipSuccess) e = dispatch<LRoundTail>(qv.dt, qv.al, qv.g_tail + qs.g_tail, pv, qs.p, (int)qv.g_tail, st);
+  if (e == hipSuccess) e = dispatch<LSampleEpi>(qs.dt, qs.al, qs.g_tail, qs.p, st);
   return hip_status(e);
 }
 
@@ -618,9 +592,7 @@ ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
     e = dispatch<LVerifyGated>(q.dt, q.al, (int64_t)p.B * (K1 - J) * nch, pg, st);
   }
   p.jn = 0;
-  p.nchunk = q.nch_accept;
-  if (e == hipSuccess) e = dispatch<LAccept>(q.dt, q.al, q.g_accept, p, st);
-  if (e == hipSuccess) e = dispatch<LResidualEpi>(q.dt, q.al, q.g_tail, p, st);
+  if (e == hipSuccess) e = dispatch<LVerifySeq>(q.dt, q.al, q.g_tail, p, st);
   return hip_status(e);
 }
 
@@ -761,7 +733,7 @@ ssd_status ssd_read_probe(const void* buf, size_t bytes, int32_t variant, uint32
 }
 
 ssd_status ssd_phase_read(int32_t kind, uint64_t* out, int64_t n) {
-  if (kind < 0 || kind > 2 || !out || n < 0 || n > (int64_t)PH_ITEMS * PH_N) return SSD_ERR_INVALID_ARG;
+  if (kind < 0 || kind > 1 || !out || n < 0 || n > (int64_t)PH_ITEMS * PH_N) return SSD_ERR_INVALID_ARG;
 #ifdef SSD_PHASES
   const hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_phase), (size_t)n * sizeof(uint64_t),
                                            (size_t)kind * PH_ITEMS * PH_N * sizeof(uint64_t));
