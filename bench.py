@@ -14,29 +14,36 @@ vocabulary), bf16 logits, T=1, F=4, C=0.5; cache budget 64 with fan-out
 ratio 0.6.  Inputs rotate over > 1 GiB of distinct sets so the 256 MB
 Infinity Cache cannot serve them.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config N] [--no-cache] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--config N] [--no-cache] [--no-cpu-baseline] [--no-early]
   python bench.py --copy-gib G   (plain device copy of G GiB, for counter calibration)
   python bench.py --read-gib G   (the library's streaming-read probe over G GiB: the read ceiling)
   python bench.py --phases       (phase timings of the epilogues; needs the instrumented libssd_phases.so)
 
+Timing: the headline steps run once eagerly (checked equal to the separate
+calls; ms_per_step_eager) and are then captured in a HIP graph and replayed
+three times, every replay checked again (ms_per_step_graph); ms_per_step is
+the faster of the two: the eager run where the host keeps ahead of the GPU,
+the replay (free of the Python binding's host path) where it does not.
+After that each entry point runs over the same steps back to back
+(sampling, verification, verification with early exit unless --no-early),
+with the library's kernel timer on, which stamps the streaming launches with
+HIP events recorded by the launch itself on the call's stream; each of those
+loops is then timed eagerly and as a HIP graph replay (every replay checked
+against the eager results), and ms_sample, ms_verify and ms_verify_early
+take the faster of the two; the headline schedule runs once more with the
+timer for the shared launch (separate passes, because the event work slows
+the step).
+
 Roofline: the dominant kernel of the headline schedule, the longer of its two
 HBM-bound launches: the shared launch k_round_mid (sampling's streaming pass
-beside the verification's residual pass) or the verification's streaming
-pass.  After the timed steps each entry point runs again over the same
-steps back to back (sampling, verification, verification with early exit),
-with the library's kernel timer on, which stamps the streaming launches
-with HIP events recorded by the launch itself on the call's stream; each of
-those loops is then captured in a HIP graph and replayed (every replay
-checked against the eager results) for the per-call times ms_sample,
-ms_verify and ms_verify_early, free of the Python binding's host path; the
-headline schedule runs once more with the timer for the shared launch
-(separate passes, because the event work slows the step).  Algorithmic bytes: B (K+1) V element bytes read + one
-16-byte partial per 2048-token block written, + for the shared launch the
-draft row k* of every sequence with a residual and the residual block sums
-(+ for the verification stream the drafted tokens and captured logits).
-`traffic` comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary committed
-under profiles/ for that kernel, and is null when the kernel sources changed
-since it was taken.
+beside the verification of each sequence) or the verification's streaming
+pass.  Algorithmic bytes: B (K+1) V element bytes read + one 16-byte partial
+per 2048-token block written (+ for the shared launch the verification's
+reads of the target partials; + for the verification stream the drafted
+tokens and captured logits); the few blocks of row k* that the lazy block
+race reads again are not counted.  `traffic` comes from the rocprofv3
+FETCH_SIZE / WRITE_SIZE summary committed under profiles/ for that kernel,
+and is null when the kernel sources changed since it was taken.
 """
 import argparse
 import hashlib
@@ -69,6 +76,9 @@ def parse():
     ap.add_argument("--read-variants", default="all")
     ap.add_argument("--read-chunk-mb", type=float, default=0.0)
     ap.add_argument("--phases", action="store_true")
+    # skip the early-exit verification (its first pass is the same kernel as
+    # the full verification stream: a clean counter profile of the latter)
+    ap.add_argument("--no-early", action="store_true")
     return ap.parse_args()
 
 
@@ -326,6 +336,34 @@ def main():
     same = bool(torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:]))
     if not same:
         raise SystemExit("ssd_round gave other accepted lengths or cache hits than the separate calls")
+    ms_eager = start.elapsed_time(stop) / a.steps
+    # the headline steps captured once in a HIP graph and replayed: the GPU's
+    # time per step, free of the binding's host path (slower than the GPU at
+    # small batches); every replay is checked against the separate calls
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # the binding's workspaces for this stream, before capture
+        run_rounds(a.warmup, total)
+    side.synchronize()
+    g_round = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_round, stream=side):
+        run_rounds(a.warmup, total)
+    side.synchronize()
+    step_ms = []
+    for rep_ in range(3):
+        acc_buf[a.warmup:].fill_(-1)
+        if use_cache:
+            hit_buf[a.warmup:].fill_(-1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            e0.record()
+            g_round.replay()
+            e1.record()
+        side.synchronize()
+        step_ms.append(e0.elapsed_time(e1) / a.steps)
+        if not (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:])):
+            raise SystemExit(f"ssd_round graph replay {rep_} gave other accepted lengths or cache hits")
     # per-call pass: each entry point over all the timed steps back to back
     # (the host enqueues ahead, so the times are the GPU's), with per-step
     # sampling outputs and cache keys, and the streaming launches stamped by
@@ -362,12 +400,12 @@ def main():
 
     def results_match():
         return (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:])
-                and torch.equal(acc_early, acc_buf[a.warmup:]))
+                and (a.no_early or torch.equal(acc_early, acc_buf[a.warmup:])))
+    loops = (loop_sample, loop_verify) if a.no_early else (loop_sample, loop_verify, loop_early)
 
     ssd.timer_enable(a.steps)
-    loop_sample()
-    loop_verify()
-    loop_early()
+    for fn in loops:
+        fn()
     torch.cuda.synchronize()
     k_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
     ssd.timer_enable(0)
@@ -376,21 +414,31 @@ def main():
     # per-call times on the GPU: each loop captured once in a HIP graph (at
     # small batches the binding's host path is slower than the GPU) and
     # replayed several times, every replay checked against the eager results
-    side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # the binding's workspaces for this stream, before capture
-        loop_sample()
-        loop_verify()
-        loop_early()
+        for fn in loops:
+            fn()
     side.synchronize()
     graphs = []
-    for fn in (loop_sample, loop_verify, loop_early):
+    for fn in loops:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             fn()
         graphs.append(g)
     side.synchronize()
-    call_ms = [[], [], []]
+    # each loop timed eagerly as well (no timer): where the host keeps ahead
+    # of the GPU this avoids the graph's own per-node cost
+    eager_ms = [[] for _ in loops]
+    for rep_ in range(3):
+        for k, fn in enumerate(loops):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            eager_ms[k].append(e0.elapsed_time(e1) / a.steps)
+    call_ms = [[] for _ in loops]
     for rep_ in range(3):
         acc_buf[a.warmup:].fill_(-1)
         acc_early.fill_(-1)
@@ -414,16 +462,25 @@ def main():
     torch.cuda.synchronize()
     r_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
     ssd.timer_enable(0)
-    ms = start.elapsed_time(stop) / a.steps
+    # per step and per call: the faster of the graph replays and the eager
+    # runs (eager where the host keeps ahead of the GPU, the graph where not)
+    med = lambda x: sorted(x)[len(x) // 2]  # (the median of three repeats drops a stray one)
+    ms_graph = med(step_ms)
+    ms = min(ms_graph, ms_eager)
     ms_sep = s0.elapsed_time(s1) / a.steps
-    t_s, t_v, t_ve = (sum(x) / len(x) for x in call_ms)
+    per_call = [min(med(g), med(e)) for g, e in zip(call_ms, eager_ms)]
+    t_s, t_v = per_call[:2]
+    t_ve = per_call[2] if len(per_call) > 2 else None
     acc = acc_buf[a.warmup:].to(torch.int64)
     tokens = int((acc + 1).sum().item())
-    # residual row pairs per step: T > 0 sequences with k* < K
+    # sequences drawing their bonus from a residual per step: T > 0, k* < K
     rej = int(((acc < K) & (T > 0).unsqueeze(0)).sum().item()) / a.steps
     row_bytes = V * esz
+    # bytes each call must read: every draft row, every target row; the
+    # residual's blocks that the lazy block race re-reads (a few per sequence,
+    # under 2% of the call) are not counted
     b_sample = cfg.rows * row_bytes
-    b_verify = cfg.rows * row_bytes + rej * row_bytes
+    b_verify = cfg.rows * row_bytes
     rows_per_s = cfg.rows / (ms * 1e-3)
     gbs_sample = b_sample / (t_s * 1e-3) / 1e9
     gbs_verify = b_verify / (t_v * 1e-3) / 1e9
@@ -434,10 +491,9 @@ def main():
     NB = -(-V // 2048)
     s_bytes = cfg.rows * row_bytes + cfg.rows * NB * 16
     v_bytes = cfg.rows * row_bytes + cfg.rows * NB * 16 + 2 * B * K * 4 + B * K * 4
-    # shared launch: sampling's stream + the draft row k* of every sequence
-    # with a residual (its target row k* is a re-read, not counted) + the
-    # residual block sums written
-    m_bytes = s_bytes + rej * row_bytes + B * NB * 8
+    # shared launch: sampling's stream + the verification role's reads of the
+    # target partials (its lazy race's block re-reads not counted)
+    m_bytes = s_bytes + cfg.rows * NB * 16
     dtn = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[cfg.dtype]
     al = "aligned" if (V * esz) % 16 == 0 else "unaligned"
     # the dominant kernel of the headline schedule: the longer of its two
@@ -487,10 +543,14 @@ def main():
         "tokens_per_s": round(tokens / (a.steps * ms * 1e-3), 1),
         "schedule": "ssd_round: step i's verification shares launches with step i+1's sampling",
         "ms_per_step_separate_calls": round(ms_sep, 5),
+        "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_graph": round(ms_graph, 5),
+        "ms_per_call_graph": [round(med(g), 5) for g in call_ms],
+        "ms_per_call_eager": [round(med(e), 5) for e in eager_ms],
         "mean_accepted": round(float(acc.float().mean().item()), 4),
         "ms_sample": round(t_s, 5),
         "ms_verify": round(t_v, 5),
-        "ms_verify_early": round(t_ve, 5),
+        "ms_verify_early": round(t_ve, 5) if t_ve is not None else None,
         "early_exit_J": EARLY_J,
         "gbs_sample": round(gbs_sample, 1),
         "gbs_verify": round(gbs_verify, 1),
@@ -511,7 +571,7 @@ def main():
         },
         "ms_round_mid": round(r_ms[ssd.OP_SAMPLE], 5),
         "ms_round_verify_stream": round(r_ms[ssd.OP_VERIFY], 5),
-        "residual_rows_per_step": round(rej, 2),
+        "residual_sequences_per_step": round(rej, 2),
         "ms_stream_sample": round(k_ms[ssd.OP_SAMPLE], 5),
         "ms_stream_verify": round(k_ms[ssd.OP_VERIFY], 5),
         "gbs_stream_sample": round(s_bytes / (k_ms[ssd.OP_SAMPLE] * 1e-3) / 1e9, 1),

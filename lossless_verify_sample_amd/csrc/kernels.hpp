@@ -27,35 +27,34 @@ namespace ssd {
 // instrumented build (-DSSD_PHASES, a measurement aid): the first lane of
 // wave 0 records the 100 MHz real-time counter at fixed points of each item
 // (kind 0: sampling epilogue, per row; kind 1: verification after the
-// streaming pass, per sequence).
+// streaming pass, per sequence).  The stamps are kept in registers and
+// stored at the end of the item, so that no stamp's store is outstanding
+// while the item waits on a load (one wait counter covers loads and stores).
 constexpr int PH_N = 8;
 constexpr int PH_ITEMS = 8192;
 #ifdef SSD_PHASES
 __device__ uint64_t g_phase[2][PH_ITEMS * PH_N];
-#define SSD_PHASE(kind, item, k)                                                              \
-  do {                                                                                        \
-    if (threadIdx.x == 0 && (int64_t)(item) < PH_ITEMS)                                       \
-      g_phase[kind][(int64_t)(item) * PH_N + (k)] = __builtin_amdgcn_s_memrealtime();          \
-  } while (0)
-// Buffered stamps (verification): kept in registers and stored at the end
-// of the item, so that no stamp's store is outstanding while the item waits
-// on a load (the wait counter counts stores too).
 #define SSD_PH_DECL uint64_t ph_[PH_N] = {}
 #define SSD_PH(k) (ph_[k] = __builtin_amdgcn_s_memrealtime())
 #define SSD_PH_SET(k, v) (ph_[k] = (uint64_t)(v))
-#define SSD_PH_FLUSH(kind, item)                                             \
-  do {                                                                       \
-    if (threadIdx.x == 0 && (int64_t)(item) < PH_ITEMS)                      \
-      for (int k_ = 0; k_ < PH_N; ++k_) g_phase[kind][(int64_t)(item) * PH_N + k_] = ph_[k_]; \
+#define SSD_PH_FLUSH(kind, item)                                                              \
+  do {                                                                                        \
+    if (threadIdx.x == 0 && (int64_t)(item) < PH_ITEMS)                                       \
+      for (int k_ = 0; k_ < PH_N; ++k_) g_phase[kind][(int64_t)(item) * PH_N + k_] = ph_[k_];  \
   } while (0)
 #else
-#define SSD_PHASE(kind, item, k) \
+#define SSD_PH_DECL \
+  do {              \
+  } while (0)
+#define SSD_PH(k) \
+  do {            \
+  } while (0)
+#define SSD_PH_SET(k, v) \
+  do {                   \
+  } while (0)
+#define SSD_PH_FLUSH(kind, item) \
   do {                           \
   } while (0)
-#define SSD_PH_DECL do {} while (0)
-#define SSD_PH(k) do {} while (0)
-#define SSD_PH_SET(k, v) do {} while (0)
-#define SSD_PH_FLUSH(kind, item) do {} while (0)
 #endif
 
 enum Mode { M_SOFTMAX = 0, M_TOPF = 1, M_SAMPLE = 2, M_VERIFY = 3 };
@@ -114,6 +113,7 @@ struct Params {
   int32_t* acc_len;
   int32_t* bonus;
   float* p_out;
+  int32_t* alive;           // early exit: 1 when a sequence has no clear rejection below the gate [B]
   // speculation cache (optional): depth offsets, keys, payload, lookup outputs
   int koff[MAX_K1 + 1];
   int Bgt;
@@ -748,7 +748,8 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   const int NB = p.NB, V = (int)p.V, F = p.F;
   const float C = p.C;
   const unsigned char* rp = p.x + row * p.ld * Dt<DT>::SZ;
-  SSD_PHASE(0, row, 0);
+  SSD_PH_DECL;
+  SSD_PH(0);
   if (tid == 0) sm.nre = 0;
   const bool draw = !greedy && j < p.K;
   WRow<PLN> r;
@@ -764,7 +765,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
 #pragma unroll
   for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
   const float m = wave_max(lm);
-  SSD_PHASE(0, row, 1);  // partials loaded, row maximum
+  SSD_PH(1);  // partials loaded, row maximum
   float w[PLN];
   double ws = 0.0;
 #pragma unroll
@@ -773,39 +774,50 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
     ws += (double)w[i];
   }
   const double tot0 = greedy ? 1.0 : wave_sum_d(ws);
-  SSD_PHASE(0, row, 2);  // block weights and their sum
+  SSD_PH(2);  // block weights and their sum
   // entries ranked: F for sigma and F_out listed; this depth's cache keys
   // when they fit in that list (longer key lists have workgroups of their own)
   const int Fj = p.ckeys ? p.koff[j + 1] - p.koff[j] : 0;
   const uint64_t tkey = wave_topf<DT, AL, PLN>(rp, V, NB, p.F_sel, r, m, sm);
-  SSD_PHASE(0, row, 3);  // top-F list
+  SSD_PH(3);  // top-F list
   const float tv = key_val(tkey);
   const int ti = (int)key_idx(tkey);
   // sigma_{F,C}: lane f < F holds 2^((z_f - m) s) of the f-th member of S
   const float es = (!greedy && lane < F) ? __builtin_amdgcn_exp2f((tv - m) * s) : 0.f;
   const double zs = wave_sum_d((double)es);
   const double lse = greedy ? 0.0 : ln_fast((tot0 - zs) + (double)C * zs);
-  if (tid < 64) {
-    if (lane < p.F_out) {
-      if (p.out_idx) p.out_idx[row * p.F_out + lane] = ti;
-      if (p.out_val) p.out_val[row * p.F_out + lane] = tv;
+  // the row's outputs are stored at the end of each path: a wait for a later
+  // load (the chosen block's) would wait for them too (one counter covers
+  // loads and stores)
+  auto store_row = [&]() {
+    if (tid < 64) {
+      if (lane < p.F_out) {
+        if (p.out_idx) p.out_idx[row * p.F_out + lane] = ti;
+        if (p.out_val) p.out_val[row * p.F_out + lane] = tv;
+      }
+      if (Fj <= p.F_sel && lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = ti;
+      if (lane == 0) {
+        ssd_row_stats st;
+        st.lse = lse;
+        st.max = m;
+        st.argmax = ti;
+        p.stats[row] = st;
+      }
     }
-    if (Fj <= p.F_sel && lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = ti;
-    if (lane == 0) {
-      ssd_row_stats st;
-      st.lse = lse;
-      st.max = m;
-      st.argmax = ti;
-      p.stats[row] = st;
-    }
+  };
+  SSD_PH(4);  // sigma normaliser
+  if (j == p.K) {  // row K only predicts the bonus after K acceptances
+    store_row();
+    SSD_PH_FLUSH(0, row);
+    return;
   }
-  SSD_PHASE(0, row, 4);  // sigma normaliser, statistics and lists written
-  if (j == p.K) return;  // row K only predicts the bonus after K acceptances
   if (greedy) {
     if (tid == 0) {
       p.tokens[b * p.K + j] = ti;
       p.q[b * p.K + j] = 1.0f;
     }
+    store_row();
+    SSD_PH_FLUSH(0, row);
     return;
   }
   // block stage (every wave): blocks holding members of S lose (1 - C) of
@@ -827,7 +839,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
   }
   bk = wave_min_u64(bk);
   const int beta = bk == NO_KEY ? 0 : (int)(uint32_t)bk;  // no block of mass only for invalid rows
-  SSD_PHASE(0, row, 5);  // block drawn
+  SSD_PH(5);  // block drawn
   // token stage over block beta
   const int x0 = beta * BLK + TPT * tid;
   Run<DT, AL> run;
@@ -843,7 +855,7 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
     if (!(z[e] > -INFINITY)) return INFINITY;
     return (Mb - z[e]) * s + (((smask >> e) & 1u) ? nc2 : 0.f);
   });
-  SSD_PHASE(0, row, 6);  // chosen block re-read and token race
+  SSD_PH(6);  // chosen block re-read and token race
   const uint32_t d = (uint32_t)(x - x0);
   if (x >= 0 && d < (uint32_t)TPT) {
     // the owner of the winning token writes it with sigma_j(x)
@@ -858,6 +870,8 @@ __device__ __forceinline__ void epi_sample_p(const Params& p, int64_t row, ESm& 
     p.tokens[b * p.K + j] = 0;
     p.q[b * p.K + j] = 0.f;
   }
+  store_row();
+  SSD_PH_FLUSH(0, row);
 }
 
 // Cache keys of depth kdep[item / B] for sequence item % B: the first F_j
@@ -1612,14 +1626,22 @@ __device__ __forceinline__ bool seq_alive(const Params& p, int b, int J, GateSm&
   return g.alive != 0;
 }
 
+// The early-exit gate, decided once per sequence (one workgroup each) over
+// the partials of positions 0 .. jlo - 1.
+template <int DT, bool AL>
+__global__ __launch_bounds__(EWG) void k_gate(Params p) {
+  __shared__ GateSm g;
+  const int b = blockIdx.x;
+  const bool alive = p.NB <= 128 ? seq_alive<2>(p, b, p.jlo, g) : seq_alive<NBL>(p, b, p.jlo, g);
+  if (threadIdx.x == 0) p.alive[b] = alive ? 1 : 0;
+}
+
 // Streaming pass of verification over positions jlo .. jlo + jn - 1, for the
-// sequences that seq_alive keeps (the others' workgroups return at once).
+// sequences the gate kept (the others' workgroups return after one load).
 template <int DT, bool AL>
 __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream_gated(Params p) {
-  __shared__ GateSm g;
   const int b = (int)((blockIdx.x / p.nchunk) / p.jn);
-  const bool alive = p.NB <= 128 ? seq_alive<2>(p, b, p.jlo, g) : seq_alive<NBL>(p, b, p.jlo, g);
-  if (!alive) return;
+  if (!p.alive[b]) return;
   stream_item<DT, AL, M_VERIFY>(p, blockIdx.x);
 }
 

@@ -33,11 +33,12 @@ int64_t nblocks(int64_t V) { return (V + BLK - 1) / BLK; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-  size_t part, zcap, total;
+  size_t part, zcap, alive, total;
 };
 
 // Workspace regions (256-byte aligned): block partials of every streamed row;
-// for verification the target logits at the drafted tokens.  Every region is written before it is read
+// for verification the target logits at the drafted tokens and the
+// early-exit gate's decisions.  Every region is written before it is read
 // within a call, so the workspace needs no initialisation.
 bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   if (n < 1 || V < 1 || V > SSD_MAX_V) return false;
@@ -49,11 +50,12 @@ bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   const int64_t NB = nblocks(V);
   const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY || op == SSD_OP_VERIFY_TREE) ? n * (K + 1) : n;
   L->part = 0;
-  L->zcap = 0;
+  L->zcap = L->alive = 0;
   size_t end = al256((size_t)(rows * NB) * sizeof(float4));
   if (op == SSD_OP_VERIFY) {
     L->zcap = end;
-    end = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
+    L->alive = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
+    end = L->alive + al256((size_t)n * sizeof(int32_t));
   }
   L->total = end;
   return true;
@@ -94,6 +96,7 @@ SSD_LAUNCHER(LTopf, (k_stream<DT, AL, M_TOPF>))
 SSD_LAUNCHER(LSample, (k_stream<DT, AL, M_SAMPLE>))
 SSD_LAUNCHER(LVerify, (k_stream<DT, AL, M_VERIFY>))
 SSD_LAUNCHER(LVerifyGated, (k_stream_gated<DT, AL>))
+SSD_LAUNCHER_E(LGate, (k_gate<DT, AL>))
 SSD_LAUNCHER_E(LSoftmaxEpi, (k_epi<DT, AL, M_SOFTMAX>))
 SSD_LAUNCHER_E(LTopfEpi, (k_epi<DT, AL, M_TOPF>))
 SSD_LAUNCHER_E(LSampleEpi, (k_epi<DT, AL, M_SAMPLE>))
@@ -297,6 +300,7 @@ ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
   p.dtok = a.draft_tokens;
   p.dq = a.draft_q;
   p.zcap = (float*)(ws + L.zcap);
+  p.alive = (int32_t*)(ws + L.alive);
   p.dstats = a.draft_stats;
   p.dtopf = F > 0 ? a.draft_topf_idx : nullptr;
   p.ld_dtopf = a.ld_topf;
@@ -578,8 +582,9 @@ ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
   if ((int64_t)q.p.B * K1 * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
-  // positions 0 .. J-1 of every sequence; then J .. K of the sequences that
-  // have no clear rejection below J; then acceptance, residual and bonus
+  // positions 0 .. J-1 of every sequence; the gate, decided once per
+  // sequence; then J .. K of the sequences with no clear rejection below J;
+  // then the verification of each sequence
   Params p = q.p;
   p.early = 1;
   p.jlo = 0;
@@ -589,7 +594,8 @@ ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
     Params pg = p;
     pg.jlo = J;
     pg.jn = K1 - J;
-    e = dispatch<LVerifyGated>(q.dt, q.al, (int64_t)p.B * (K1 - J) * nch, pg, st);
+    e = dispatch<LGate>(q.dt, q.al, (int64_t)p.B, pg, st);
+    if (e == hipSuccess) e = dispatch<LVerifyGated>(q.dt, q.al, (int64_t)p.B * (K1 - J) * nch, pg, st);
   }
   p.jn = 0;
   if (e == hipSuccess) e = dispatch<LVerifySeq>(q.dt, q.al, q.g_tail, p, st);
