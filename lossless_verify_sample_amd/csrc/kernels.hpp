@@ -1688,6 +1688,27 @@ __global__ __launch_bounds__(EWG, (DT == SSD_F32 || !AL) ? 3 : 4) void k_round_m
   else stream_item<DT, AL, M_SAMPLE>(ps, (int)blockIdx.x - nv);
 }
 
+// Small batches: a round in two launches instead, (1) both streaming passes
+// (round i's target rows, below nv; round i + 1's draft rows), (2) the
+// verification of each sequence of round i beside round i + 1's sampling
+// epilogue (below nv: the verification).
+template <int DT, bool AL>
+__global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_round_streams(Params pv, Params ps, int nv) {
+  if ((int)blockIdx.x < nv) stream_item<DT, AL, M_VERIFY>(pv, blockIdx.x);
+  else stream_item<DT, AL, M_SAMPLE>(ps, (int)blockIdx.x - nv);
+}
+
+union TailSm {
+  VSm v;
+  ESm e;
+};
+template <int DT, bool AL>
+__global__ __launch_bounds__(EWG) void k_round_tails(Params pv, Params ps, int nv) {
+  __shared__ TailSm sm;
+  if ((int)blockIdx.x < nv) verify_item<DT, AL>(pv, blockIdx.x, sm.v);
+  else sample_epi_item<DT, AL>(ps, (int)blockIdx.x - nv, sm.e);
+}
+
 // ---------------------------------------------------------------------------
 // Token-tree verification: recursive rejection sampling over the drafted
 // children of each node (the residual renormalised after each rejected

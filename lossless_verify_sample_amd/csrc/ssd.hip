@@ -121,6 +121,20 @@ struct LTree {
     }                                                                                     \
   };
 SSD_LAUNCHER2(LRoundMid, (k_round_mid<DT, AL>))
+SSD_LAUNCHER2(LRoundTails, (k_round_tails<DT, AL>))
+// (the streams' launch runs WG threads per workgroup)
+template <int DT, bool AL>
+struct LRoundStreams {
+  static hipError_t go(int64_t grid, const Params& pv, const Params& ps, int nv, hipStream_t st, hipEvent_t e0 = nullptr,
+                       hipEvent_t e1 = nullptr) {
+    if (e0) {
+      hipExtLaunchKernelGGL((k_round_streams<DT, AL>), dim3((unsigned)grid), dim3(WG), 0, st, e0, e1, 0, pv, ps, nv);
+    } else {
+      k_round_streams<DT, AL><<<dim3((unsigned)grid), dim3(WG), 0, st>>>(pv, ps, nv);
+    }
+    return hipGetLastError();
+  }
+};
 // The same with the timer's events recorded by the launch.
 template <int DT, bool AL>
 struct LRoundMidT {
@@ -144,6 +158,11 @@ const int64_t kMaxGrid = 0x7fffffff;
 // measured about 1 us less per step at B=64, K=7, V=151936 (39 MB); at 131
 // and 311 MB the shared launch slowed by 10-15%.
 constexpr int kKeepRows = 2;
+// ssd_round runs in two launches (both streaming passes, then the
+// verification beside the sampling epilogue) while the sampling's rows are
+// at most this many: at small batches the verification of a sequence takes
+// longer than the sampling's streaming pass it would otherwise share.
+constexpr int64_t kTwoLaunchRows = 256;
 constexpr int64_t kKeepBytes = int64_t(64) << 20;
 
 // Depth offsets of a cache descriptor into p (false for a bad fan-out).
@@ -336,7 +355,9 @@ ssd_status plan_round(const ssd_verify_args* v, const ssd_sample_args* s, Plan& 
     if (e != SSD_OK) return e;
   }
   if (v && s && (v->workspace == s->workspace)) return SSD_ERR_WORKSPACE;
-  if (v && s && qv.g_tail + qs.g_stream > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  if (v && s && (qv.g_tail + qs.g_stream > kMaxGrid || qv.g_stream + qs.g_stream > kMaxGrid ||
+                 qv.g_tail + qs.g_tail > kMaxGrid))
+    return SSD_ERR_UNSUPPORTED;
   if (v && s) {
     // round i+1's sampling must not write what round i's verification reads
     const void* w[] = {s->out_tokens, s->out_q, s->out_stats, s->out_topf_idx};
@@ -362,13 +383,22 @@ ssd_status launch_round(const Plan* pqv, const Plan* pqs, hipStream_t st) {
     if (e == hipSuccess) e = launch_sample(qs, st);
     return hip_status(e);
   }
+  Params pv = qv.p;
+  const int64_t nv = qv.g_tail;
+  if (qs.p.rows <= kTwoLaunchRows) {
+    // both streaming passes in one launch; then the verification of each
+    // sequence beside sampling's epilogue
+    hipError_t e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
+      return dispatch<LRoundStreams>(qv.dt, qv.al, qv.g_stream + qs.g_stream, pv, qs.p, (int)qv.g_stream, st, e0, e1);
+    });
+    if (e == hipSuccess) e = dispatch<LRoundTails>(qv.dt, qv.al, nv + qs.g_tail, pv, qs.p, (int)nv, st);
+    return hip_status(e);
+  }
   // verification's streaming pass; then the verification of each sequence
   // beside sampling's streaming pass; then sampling's epilogue
-  Params pv = qv.p;
   hipError_t e = timed(SSD_OP_VERIFY, [&](hipEvent_t e0, hipEvent_t e1) {
     return dispatch<LVerify>(qv.dt, qv.al, qv.g_stream, pv, st, e0, e1);
   });
-  const int64_t nv = qv.g_tail;
   if (e == hipSuccess) {
     e = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
       return e0 ? dispatch<LRoundMidT>(qv.dt, qv.al, nv + qs.g_stream, pv, qs.p, (int)nv, st, e0, e1)
