@@ -272,6 +272,11 @@ def main():
     total = a.warmup + a.steps
     acc_buf = torch.zeros((total, B), dtype=torch.int32, device=dev)
     hit_buf = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    # every step's bonus, p_j(x_j) and gathered cache tokens are kept, so the
+    # timed schedules' outputs are checked against the separate calls' in full
+    bonus_buf = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    p_buf = torch.zeros((total, B, K), dtype=torch.float32, device=dev)
+    tok_buf = torch.zeros((total, B, K), dtype=torch.int32, device=dev)
     def smp_buffers():
         return dict(tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
                     q=torch.empty((B, K), dtype=torch.float32, device=dev),
@@ -281,16 +286,15 @@ def main():
 
     smp_bufs = [smp_buffers(), smp_buffers()]  # the sampling of step i + 1 beside step i's verification
     smp_out = smp_bufs[0]
-    bonus = torch.empty(B, dtype=torch.int32, device=dev)
-    pout = torch.empty((B, K), dtype=torch.float32, device=dev)
     def step(i):
         t, d = sets[i % nsets]
         seed = W.seed(cfg, i)
         cache = caches[i % nsets] if use_cache else None
         if cache is not None:
             cache.hit = hit_buf[i]
+            cache.tokens = tok_buf[i]
         ssd.saguaro_sample(d, T, cfg.F, cfg.C, seed, F_out=Fo, out=smp_out, cache=cache)
-        ver_out = dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None)
+        ver_out = dict(accept_len=acc_buf[i], bonus=bonus_buf[i], p=p_buf[i], stats=None)
         ssd.verify(t, d, T, cfg.F, cfg.C, seed, smp_out["tokens"], smp_out["q"], smp_out["stats"],
                    smp_out["topf_idx"], out=ver_out, cache=cache)
 
@@ -308,9 +312,10 @@ def main():
         cache = caches[i % nsets] if use_cache else None
         if cache is not None:
             cache.hit = hit_buf[i]
+            cache.tokens = tok_buf[i]
         return dict(target=t, draft=d, temperature=T, F=cfg.F, C=cfg.C, seed=W.seed(cfg, i), tokens=smp["tokens"],
                     draft_q=smp["q"], draft_stats=smp["stats"], draft_topf_idx=smp["topf_idx"],
-                    out=dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None), cache=cache)
+                    out=dict(accept_len=acc_buf[i], bonus=bonus_buf[i], p=p_buf[i], stats=None), cache=cache)
 
     def run_rounds(lo, hi):
         ssd.round_step(None, sample_args(lo))
@@ -329,16 +334,32 @@ def main():
     torch.cuda.synchronize()
     acc_sep = acc_buf[a.warmup:].clone()
     hit_sep = hit_buf[a.warmup:].clone()
+    outs_sep = [x[a.warmup:].clone() for x in (bonus_buf, p_buf, tok_buf)]
+
+    def same_outputs():
+        # accepted lengths, bonus, p_j(x_j), hits and gathered tokens of every
+        # timed step equal to the separate calls' (bit for bit)
+        ok = (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(outs_sep[0], bonus_buf[a.warmup:])
+              and torch.equal(outs_sep[1], p_buf[a.warmup:]))
+        if use_cache:
+            ok = ok and torch.equal(hit_sep, hit_buf[a.warmup:]) and torch.equal(outs_sep[2], tok_buf[a.warmup:])
+        return ok
+
+    def clear_outputs():
+        for x in (acc_buf, bonus_buf) + ((hit_buf, tok_buf) if use_cache else ()):
+            x[a.warmup:].fill_(-1)
+        p_buf[a.warmup:].fill_(-1.0)
     run_rounds(0, a.warmup)
+    torch.cuda.synchronize()
+    clear_outputs()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     run_rounds(a.warmup, total)
     stop.record()
     torch.cuda.synchronize()
-    same = bool(torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:]))
-    if not same:
-        raise SystemExit("ssd_round gave other accepted lengths or cache hits than the separate calls")
+    if not same_outputs():
+        raise SystemExit("ssd_round gave other outputs than the separate calls")
     ms_eager = start.elapsed_time(stop) / a.steps
     # the headline steps captured once in a HIP graph and replayed: the GPU's
     # time per step, free of the binding's host path (slower than the GPU at
@@ -354,9 +375,7 @@ def main():
     side.synchronize()
     step_ms = []
     for rep_ in range(3):
-        acc_buf[a.warmup:].fill_(-1)
-        if use_cache:
-            hit_buf[a.warmup:].fill_(-1)
+        clear_outputs()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(side):
@@ -365,8 +384,8 @@ def main():
             e1.record()
         side.synchronize()
         step_ms.append(e0.elapsed_time(e1) / a.steps)
-        if not (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:])):
-            raise SystemExit(f"ssd_round graph replay {rep_} gave other accepted lengths or cache hits")
+        if not same_outputs():
+            raise SystemExit(f"ssd_round graph replay {rep_} gave other outputs than the separate calls")
     # per-call pass: each entry point over all the timed steps back to back
     # (the host enqueues ahead, so the times are the GPU's), with per-step
     # sampling outputs and cache keys, and the streaming launches stamped by
@@ -378,8 +397,8 @@ def main():
     caches_t = ([ssd.Cache(Fk, B, K, dev, payload=caches[i % nsets].payload, miss_fill=True) for i in timed]
                 if use_cache else [None] * a.steps)
     acc_early = torch.zeros((a.steps, B), dtype=torch.int32, device=dev)
-    out_early = dict(bonus=torch.empty(B, dtype=torch.int32, device=dev),
-                     p=torch.empty((B, K), dtype=torch.float32, device=dev), stats=None)
+    bonus_early = torch.zeros((a.steps, B), dtype=torch.int32, device=dev)
+    p_early = torch.empty((B, K), dtype=torch.float32, device=dev)  # (NaN past k*: not compared)
     def loop_sample():
         for n, i in enumerate(timed):
             ssd.saguaro_sample(sets[i % nsets][1], T, cfg.F, cfg.C, W.seed(cfg, i), F_out=Fo, out=smp_all[n],
@@ -391,19 +410,21 @@ def main():
             sm = smp_all[n]
             if caches_t[n] is not None:
                 caches_t[n].hit = hit_buf[i]
+                caches_t[n].tokens = tok_buf[i]
             ssd.verify(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"], sm["topf_idx"],
-                       out=dict(accept_len=acc_buf[i], bonus=bonus, p=pout, stats=None), cache=caches_t[n])
+                       out=dict(accept_len=acc_buf[i], bonus=bonus_buf[i], p=p_buf[i], stats=None), cache=caches_t[n])
 
     def loop_early():
         for n, i in enumerate(timed):
             t, d = sets[i % nsets]
             sm = smp_all[n]
             ssd.verify_early(t, d, T, cfg.F, cfg.C, W.seed(cfg, i), sm["tokens"], sm["q"], sm["stats"],
-                             sm["topf_idx"], J=EARLY_J, out=dict(out_early, accept_len=acc_early[n]))
+                             sm["topf_idx"], J=EARLY_J,
+                             out=dict(accept_len=acc_early[n], bonus=bonus_early[n], p=p_early, stats=None))
 
     def results_match():
-        return (torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(hit_sep, hit_buf[a.warmup:])
-                and (a.no_early or torch.equal(acc_early, acc_buf[a.warmup:])))
+        return same_outputs() and (a.no_early or (torch.equal(acc_early, acc_sep)
+                                                  and torch.equal(bonus_early, outs_sep[0])))
     loops = (loop_sample, loop_verify) if a.no_early else (loop_sample, loop_verify, loop_early)
 
     ssd.timer_enable(a.steps)
@@ -413,7 +434,7 @@ def main():
     k_launch = {op: ssd.timer_read(op) for op in (ssd.OP_SAMPLE, ssd.OP_VERIFY)}
     ssd.timer_enable(0)
     if not results_match():
-        raise SystemExit("the per-call pass or ssd_verify_early gave other accepted lengths or cache hits")
+        raise SystemExit("the per-call pass or ssd_verify_early gave other outputs than the separate calls")
     # per-call times on the GPU: each loop captured once in a HIP graph (at
     # small batches the binding's host path is slower than the GPU) and
     # replayed several times, every replay checked against the eager results
@@ -443,10 +464,9 @@ def main():
             eager_ms[k].append(e0.elapsed_time(e1) / a.steps)
     call_ms = [[] for _ in loops]
     for rep_ in range(3):
-        acc_buf[a.warmup:].fill_(-1)
+        clear_outputs()
         acc_early.fill_(-1)
-        if use_cache:  # (written only by the cache lookup)
-            hit_buf[a.warmup:].fill_(-1)
+        bonus_early.fill_(-1)
         torch.cuda.synchronize()
         for k, g in enumerate(graphs):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -457,9 +477,9 @@ def main():
             side.synchronize()
             call_ms[k].append(e0.elapsed_time(e1) / a.steps)
         if not results_match():
-            raise SystemExit(f"graph replay {rep_} gave other accepted lengths or cache hits")
+            raise SystemExit(f"graph replay {rep_} gave other outputs than the separate calls")
     # and the headline schedule once more with the timer: there the sampling
-    # op is the shared launch (sampling stream + residual pass)
+    # op is the shared launch (sampling stream + verification of each sequence)
     ssd.timer_enable(a.steps + 1)
     run_rounds(a.warmup, total)
     torch.cuda.synchronize()
