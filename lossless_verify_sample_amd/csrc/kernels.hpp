@@ -1029,12 +1029,14 @@ struct CacheRegs {
   bool ok;
   int key;
   int pay[KREG];
+  int fb;  // lane i < K: fallback token i of a miss (when filled), or -1 to draw it at the lookup
 };
 
 __device__ __forceinline__ void cache_prefetch(const Params& p, int b, CacheRegs& cr) {
   const int lane = threadIdx.x & 63, K = p.K, Bgt = p.Bgt;
   cr.ok = p.lookup && Bgt <= 64 && K <= KREG;
   cr.key = 0;
+  cr.fb = -1;
 #pragma unroll
   for (int i = 0; i < KREG; ++i) cr.pay[i] = -1;
   if (!cr.ok || threadIdx.x >= 64 || lane >= Bgt) return;
@@ -1067,7 +1069,7 @@ __device__ __forceinline__ void cache_lookup_wave(const Params& p, int b, int k,
         t = lane == i ? v : t;
       }
     } else if (p.fill && lane < K) {
-      t = fallback_token(p.seed, b, lane, p.V);
+      t = cr.fb >= 0 ? cr.fb : fallback_token(p.seed, b, lane, p.V);
     }
     if (lane < K) p.ctok[(int64_t)b * K + lane] = t;
     return;
@@ -1127,6 +1129,7 @@ struct VSm {
   int tf[TF_CAP];           // the draft top-F lists of the sequence's rows
   int ckey[64];             // the sequence's cache keys and payload when they fit (CacheRegs)
   int cpay[64 * KREG];
+  int cfb[64];              // the fallback tokens of a miss
   int ks;
   SeqState ss;
   float vm[MAX_K1];
@@ -1186,25 +1189,8 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
   // stay there with, for rows j < K of T > 0 sequences, the lazy race's
   // block draws (carried by the partials) and bounds.
   const bool pre = fit && !greedy;
-  auto merge = [&](const WRow<PLN>& r, int j) {
-    float lm = r.M[0];
-#pragma unroll
-    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
-    const float m = wave_max(lm);
-    int fb = -1, am = -1;
-    double wsum = 0.0;
-    float W[PLN];
-#pragma unroll
-    for (int i = PLN - 1; i >= 0; --i) {
-      W[i] = greedy ? 0.f : block_w(r.M[i], r.S[i], m, s);
-      wsum += (double)W[i];
-      const uint64_t mk = __ballot(lane + 64 * i < NB && r.M[i] == m);
-      if (mk) {
-        fb = 64 * i + (int)__builtin_ctzll(mk);
-        am = __builtin_amdgcn_readlane(r.I[i], (int)__builtin_ctzll(mk));
-      }
-    }
-    wsum = wave_sum_d(wsum);
+  // a row's values after the reductions, kept in LDS
+  auto keep = [&](const WRow<PLN>& r, int j, float m, double wsum, const float (&W)[PLN], int fb, int am) {
     if (pre) {
 #pragma unroll
       for (int i = 0; i < PLN; ++i) {
@@ -1227,24 +1213,64 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
       sm.vam[j] = greedy ? (am < 0 ? 0 : am) : -1;  // greedy rows carry the block argmax in their partial
     }
   };
+  // rows ja and jb (jb kept when hb) merged stage by stage, so that the two
+  // rows' wave reductions overlap
+  auto merge2 = [&](const WRow<PLN>& ra, int ja, const WRow<PLN>& rb, int jb, bool hb) {
+    float la = ra.M[0], lb = rb.M[0];
+#pragma unroll
+    for (int i = 1; i < PLN; ++i) {
+      la = fmaxf(la, ra.M[i]);
+      lb = fmaxf(lb, rb.M[i]);
+    }
+    const float ma = wave_max(la), mb = wave_max(lb);
+    int fba = -1, ama = -1, fbb = -1, amb = -1;
+    double sa = 0.0, sb = 0.0;
+    float Wa[PLN], Wb[PLN];
+#pragma unroll
+    for (int i = PLN - 1; i >= 0; --i) {
+      Wa[i] = greedy ? 0.f : block_w(ra.M[i], ra.S[i], ma, s);
+      Wb[i] = greedy ? 0.f : block_w(rb.M[i], rb.S[i], mb, s);
+      sa += (double)Wa[i];
+      sb += (double)Wb[i];
+      const uint64_t ka = __ballot(lane + 64 * i < NB && ra.M[i] == ma);
+      const uint64_t kb = __ballot(lane + 64 * i < NB && rb.M[i] == mb);
+      if (ka) {
+        fba = 64 * i + (int)__builtin_ctzll(ka);
+        ama = __builtin_amdgcn_readlane(ra.I[i], (int)__builtin_ctzll(ka));
+      }
+      if (kb) {
+        fbb = 64 * i + (int)__builtin_ctzll(kb);
+        amb = __builtin_amdgcn_readlane(rb.I[i], (int)__builtin_ctzll(kb));
+      }
+    }
+    sa = wave_sum_d(sa);
+    sb = wave_sum_d(sb);
+    keep(ra, ja, ma, sa, Wa, fba, ama);
+    if (hb) keep(rb, jb, mb, sb, Wb, fbb, amb);
+  };
   float uacc = 0.f;
+  int fbt = -1;
   for (int j0 = wave; j0 < K1; j0 += 2 * ENW) {
     const int j1 = j0 + ENW;
     WRow<PLN> ra, rb;
     load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
     load_wrow<PLN>(p.part + (r0 + min(j1, K)) * NB, NB, rb);
-    // wave 0, lane j: the acceptance draw u_j, computed while the partials load
-    if (wave == 0 && j0 == 0 && !greedy)
-      uacc = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
-    merge(ra, j0);
-    if (j1 < K1) merge(rb, j1);
+    // wave 0, lane j: the acceptance draw u_j and the fallback token j of a
+    // cache miss, computed while the partials load
+    if (wave == 0 && j0 == 0) {
+      if (!greedy) uacc = uniform_of(draw1(p.seed, 0u, (uint32_t)b, (uint32_t)lane, ST_ACCEPT));
+      if (cr.ok && p.fill && lane < K) fbt = fallback_token(p.seed, b, lane, p.V);
+    }
+    merge2(ra, j0, rb, j1, j1 < K1);
   }
   if (tf_lds && tid < K1 * F) sm.tf[tid] = tfv;
-  // the cache keys and payload wait in LDS (registers are short later on)
+  // the cache keys and payload wait in LDS (registers are short later on),
+  // with the fallback tokens of a miss (drawn while the partials loaded)
   if (cr.ok && tid < 64) {
     sm.ckey[lane] = cr.key;
 #pragma unroll
     for (int i = 0; i < KREG; ++i) sm.cpay[lane * KREG + i] = cr.pay[i];
+    sm.cfb[lane] = fbt;
   }
   lds_sync();
   SSD_PH(1);  // prologue loads and the K+1 rows' statistics
@@ -1266,9 +1292,10 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
         pj = acc ? 1.0 : 0.0;
       } else {
         pj = exp_fast(((double)ztj - (double)sm.vm[lane]) * invT - sm.vL[lane]);
+        // u < p / q taken as u q < p (q > 0): the two differ only where u
+        // and p / q agree to the last bits of fp64, a near tie
         const double q = (double)qj;
-        const double rho = q > 0.0 ? pj / q : (pj > 0.0 ? INFINITY : 0.0);
-        acc = (double)uacc < rho;
+        acc = q > 0.0 ? (double)uacc * q < pj : pj > 0.0;
       }
     }
     const uint64_t rej = __ballot(lane < K && !acc);
@@ -1458,6 +1485,7 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
     CacheRegs c2;
     c2.ok = cr.ok;
     c2.key = cr.ok ? sm.ckey[lane] : 0;
+    c2.fb = cr.ok ? sm.cfb[lane] : -1;
 #pragma unroll
     for (int i = 0; i < KREG; ++i) c2.pay[i] = cr.ok ? sm.cpay[lane * KREG + i] : -1;
     cache_lookup_wave(p, b, ks, y, c2);
