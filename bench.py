@@ -59,6 +59,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD specification
 # ssd_round's schedule: while B (K+1) <= this, two launches (both streaming
 # passes, then the verification beside the sampling epilogue), else three
+ARITH_DTYPE = "f32"  # every input type is decoded to fp32 for the streaming arithmetic
 ROUND_TWO_LAUNCH_ROWS = 256
 EARLY_J = 2            # positions streamed for every sequence by ssd_verify_early
 
@@ -562,7 +563,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the arithmetic of the path: fp32 streaming sums and races over the
+        # decoded logits (fp64 row normalisers and acceptance tests)
+        "dtype": ARITH_DTYPE,
+        "input_dtype": dtn,
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={B} K={K} V={V} {str(cfg.dtype).split('.')[-1]} logits, "
                                f"T={cfg.T} F={cfg.F} C={cfg.C}"

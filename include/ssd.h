@@ -519,11 +519,13 @@ ssd_status ssd_phase_read(int32_t kind, uint64_t* out, int64_t n);
  * ssd_verify -- is timed by a pair of HIP events that the launch itself
  * records on the call's stream (hipExtLaunchKernelGGL), up to max_launches
  * launches per op.  In ssd_round the launch that carries the sampling's
- * streaming pass (beside the verification's residual pass) counts as
- * SSD_OP_SAMPLE and the verification's streaming pass as SSD_OP_VERIFY.
+ * streaming pass (beside the verification of each sequence, or at small
+ * batches beside the verification's streaming pass) counts as SSD_OP_SAMPLE
+ * and a launch of the verification's streaming pass alone as SSD_OP_VERIFY.
  *   ssd_timer_enable(n): n > 0 (re)creates the events and clears the counts;
- *     n = 0 destroys them.  Host-side state of the library, not thread-safe:
- *     enable, read and disable from one thread while no call is in flight.
+ *     n = 0 destroys them.  Host-side state of the library, guarded by a
+ *     mutex; launches from several threads interleave in one count, so time
+ *     one thread's calls at a time.
  *     Errors: n < 0 or n > 1 << 20 (INVALID_ARG), event creation (HIP).
  *   ssd_timer_read(op, &launches, &total_ms): waits for the recorded events
  *     and returns how many launches of that op were timed and their summed

@@ -179,13 +179,16 @@ bool cache_layout(const ssd_cache* c, int K, int64_t V, Params& p) {
   return true;
 }
 
-// Kernel timer: event pairs around the streaming-pass launches, per op.
+// Kernel timer: event pairs around the streaming-pass launches, per op
+// (host state, guarded by a mutex: calls from several threads stay safe, the
+// counts then mix their launches).
 struct Timer {
   int cap = 0;
   int n[4] = {0, 0, 0, 0};
   std::vector<hipEvent_t> ev[4];
 };
 Timer g_timer;
+std::mutex g_timer_mu;
 
 void timer_free() {
   for (auto& v : g_timer.ev) {
@@ -200,6 +203,7 @@ void timer_free() {
 // pair when it is enabled and has room, else with none.
 template <class F>
 hipError_t timed(ssd_op op, F launch) {
+  std::lock_guard<std::mutex> lock(g_timer_mu);
   if (g_timer.cap > 0 && g_timer.n[op] < g_timer.cap) {
     const int i = g_timer.n[op];
     const hipError_t e = launch(g_timer.ev[op][2 * i], g_timer.ev[op][2 * i + 1]);
@@ -781,6 +785,7 @@ ssd_status ssd_phase_read(int32_t kind, uint64_t* out, int64_t n) {
 
 ssd_status ssd_timer_enable(int32_t max_launches) {
   if (max_launches < 0 || max_launches > (1 << 20)) return SSD_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_timer_mu);
   timer_free();
   if (max_launches == 0) return SSD_OK;
   for (auto& v : g_timer.ev) {
@@ -799,6 +804,7 @@ ssd_status ssd_timer_enable(int32_t max_launches) {
 
 ssd_status ssd_timer_read(ssd_op op, int32_t* launches, double* total_ms) {
   if (op < SSD_OP_SOFTMAX_T || op > SSD_OP_VERIFY || !launches || !total_ms) return SSD_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_timer_mu);
   double t = 0.0;
   for (int i = 0; i < g_timer.n[op]; ++i) {
     float ms = 0.f;
