@@ -75,6 +75,44 @@ def test_neg_inf_and_ties():
     assert rep.ok(), rep.fails
 
 
+def test_lazy_block_race_edge_cases():
+    """The bonus's lazy block race on rows built against it: (a) the block of
+    largest target mass has no residual (the draft covers it alone), the
+    residual is spread over many blocks of small mass, some blocks of the
+    target are -inf (zero mass: evaluated only while no mass is found);
+    (b) the residual sits in the ragged last block, which the draft misses;
+    (c) target and draft equal but for one block (tiny residual).  Against
+    the oracle, which draws the bonus from the full residual."""
+    rep = Report()
+    for step in range(4):
+        g = torch.Generator(device=DEV).manual_seed(500 + step)
+        B, K, V = 6, 3, 20 * 2048 + 777
+        base = torch.randn((B, K + 1, V), generator=g, device=DEV)
+        # (a)
+        t = base.clone()
+        t[..., :2048] += 3.0
+        t[..., 2048 * 5:2048 * 7] = -math.inf
+        d = torch.full_like(t, -math.inf)
+        d[..., :2048] = base[..., :2048] + 3.0 + 0.05 * torch.randn((B, K + 1, 2048), generator=g, device=DEV)
+        # (b)
+        tb = base.clone()
+        tb[..., 20 * 2048:] += 4.0
+        db = base.clone()
+        db[..., 20 * 2048:] = -math.inf
+        # (c)
+        tc = base.clone()
+        dc = base.clone()
+        dc[..., 2048 * 9:2048 * 10] += 0.3
+        for (tt, dd, tag) in ((t, d, "a"), (tb, db, "b"), (tc, dc, "c")):
+            for dt in (BF16, F32):
+                T = torch.tensor([1.0, 0.7, 1.3, 1.0, 0.0, 2.0], device=DEV)
+                _say(f"lazy race case {tag} step {step} {dt}")
+                r, g_s, g_v, *_ = check_round(tt.to(dt), dd.to(dt), T, 4, 0.5, 900 + step, F_out=4, workers=1)
+                rep.add(r)
+    assert rep.ok(), rep.fails
+    _say(f"units {rep.units} near-ties {rep.near}")
+
+
 def test_topf_tie_overflow_path():
     """Constant rows: every block ties at the threshold, the candidate list
     overflows and the exact fallback selection runs."""
