@@ -318,10 +318,10 @@ def main():
                     draft_q=smp["q"], draft_stats=smp["stats"], draft_topf_idx=smp["topf_idx"],
                     out=dict(accept_len=acc_buf[i], bonus=bonus_buf[i], p=p_buf[i], stats=None), cache=cache)
 
-    def run_rounds(lo, hi):
+    def run_rounds(lo, hi, early_J=None):
         ssd.round_step(None, sample_args(lo))
         for i in range(lo, hi):
-            ssd.round_step(verify_args(i), sample_args(i + 1) if i + 1 < hi else None)
+            ssd.round_step(verify_args(i), sample_args(i + 1) if i + 1 < hi else None, early_J=early_J)
 
     # the same steps with separate calls (sample, then verify)
     for i in range(a.warmup):
@@ -479,6 +479,27 @@ def main():
             call_ms[k].append(e0.elapsed_time(e1) / a.steps)
         if not results_match():
             raise SystemExit(f"graph replay {rep_} gave other outputs than the separate calls")
+    # the same steps with early-exit verification (ssd_round_early): timed
+    # eagerly (median of three), accepted lengths, bonus, hits and gathered
+    # tokens checked against the separate calls (p is NaN past k* there)
+    ms_early = None
+    if not a.no_early:
+        ems = []
+        for rep_ in range(3):
+            clear_outputs()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run_rounds(a.warmup, total, early_J=EARLY_J)
+            e1.record()
+            torch.cuda.synchronize()
+            ems.append(e0.elapsed_time(e1) / a.steps)
+            ok = torch.equal(acc_sep, acc_buf[a.warmup:]) and torch.equal(outs_sep[0], bonus_buf[a.warmup:])
+            if use_cache:
+                ok = ok and torch.equal(hit_sep, hit_buf[a.warmup:]) and torch.equal(outs_sep[2], tok_buf[a.warmup:])
+            if not ok:
+                raise SystemExit("ssd_round_early gave other outputs than the separate calls")
+        ms_early = sorted(ems)[1]
     # and the headline schedule once more with the timer: there the sampling
     # op is the shared launch (sampling stream + verification of each sequence)
     ssd.timer_enable(a.steps + 1)
@@ -581,6 +602,7 @@ def main():
         "ms_per_step_separate_calls": round(ms_sep, 5),
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": round(ms_graph, 5),
+        "ms_per_step_early_exit": round(ms_early, 5) if ms_early is not None else None,
         "ms_per_call_graph": [round(med(g), 5) for g in call_ms],
         "ms_per_call_eager": [round(med(e), 5) for e in eager_ms],
         "mean_accepted": round(float(acc.float().mean().item()), 4),

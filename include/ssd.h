@@ -300,6 +300,19 @@ ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream);
  * kind or both use the same cache keys (other aliasing is not detected). */
 ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream);
 
+/* One pipeline step with early-exit verification: ssd_round whose
+ * verification is that of ssd_verify_early (target positions J .. K read
+ * only for the sequences with no clear rejection below J; 1 <= J <= K+1).
+ * For callers that need no p_j(x_j) past the first rejection: accepted
+ * lengths, bonus tokens, cache lookup and every sampling output are those
+ * of ssd_verify_early followed by ssd_saguaro_sample on the same arguments;
+ * out_p is NaN past k* and out_target_stats must be NULL.  At large batches
+ * most target rows past the first two positions are never read; at B (K+1)
+ * <= 256 rows, or when the two calls' element types or alignments differ,
+ * the two calls run in turn.  Errors: as ssd_round, and SSD_ERR_INVALID_ARG
+ * for J outside [1, K+1] or out_target_stats not NULL. */
+ssd_status ssd_round_early(const ssd_verify_args* v, const ssd_sample_args* s, int32_t J, void* stream);
+
 /* ssd_round for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation): the
  * same arguments, checks and results as ssd_round, except that the

@@ -128,6 +128,7 @@ def _load():
         "ssd_backoff": [_vp, _i32, _vp, _vp, _vp],
         "ssd_round": [_vp, _vp, _vp],
         "ssd_round_noalloc": [_vp, _vp, _vp],
+        "ssd_round_early": [_vp, _vp, _i32, _vp],
         "ssd_verify_early": [_vp, _i32, _vp],
         "ssd_verify_tree": [_vp, _vp],
         "ssd_fanout_greedy": [_vp, _vp, _i32, _i32, _i32, _vp],
@@ -482,7 +483,7 @@ def verify_tree(target, draft, temperature, F, C, seed, parent, tokens, draft_q,
     return out
 
 
-def round_step(verify_args=None, sample_args=None, noalloc=False):
+def round_step(verify_args=None, sample_args=None, noalloc=False, early_J=None):
     """One pipeline step (ssd_round): verification of round i and draft
     sampling of round i + 1, each given as a dict of the keyword arguments of
     verify() / saguaro_sample() (with their positional ones under the same
@@ -490,8 +491,11 @@ def round_step(verify_args=None, sample_args=None, noalloc=False):
     sampling's outputs must not be the verification's inputs.  With
     noalloc=True the step runs through ssd_round_noalloc on the library's own
     scratch (no workspace is passed; outputs the caller does not give are
-    still allocated here).  Returns (verify outputs or None, sample outputs
-    or None)."""
+    still allocated here).  With early_J the verification exits early
+    (ssd_round_early, as verify_early: p is NaN past the accepted length).
+    Returns (verify outputs or None, sample outputs or None)."""
+    if early_J is not None and noalloc:
+        raise SSDError("round_step: early exit runs on a caller workspace only")
     keep = []
     vo = so = None
     vs = ss = None
@@ -504,9 +508,13 @@ def round_step(verify_args=None, sample_args=None, noalloc=False):
     if vs is None and ss is None:
         raise SSDError("round_step needs a verification or a sampling")
     dev = (verify_args["target"] if verify_args is not None else sample_args["draft"]).device
+    va = ctypes.byref(vs) if vs is not None else None
+    sa = ctypes.byref(ss) if ss is not None else None
+    if early_J is not None:
+        _check(_lib.ssd_round_early(va, sa, int(early_J), _stream(dev)), "ssd_round_early")
+        return vo, so
     fn, name = (_lib.ssd_round_noalloc, "ssd_round_noalloc") if noalloc else (_lib.ssd_round, "ssd_round")
-    _check(fn(ctypes.byref(vs) if vs is not None else None, ctypes.byref(ss) if ss is not None else None,
-              _stream(dev)), name)
+    _check(fn(va, sa, _stream(dev)), name)
     return vo, so
 
 

@@ -605,20 +605,20 @@ ssd_status ssd_verify(const void* target_logits, const void* draft_logits, ssd_d
   return hip_status(launch_verify(q, (hipStream_t)stream));
 }
 
-ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
-  if (!a) return SSD_ERR_INVALID_ARG;
-  Plan q;
-  const ssd_status s = plan_verify(*a, q);
-  if (s != SSD_OK) return s;
+// Checks of an early-exit verification on its plan.
+ssd_status check_early(const Plan& q, const ssd_verify_args& a, int32_t J) {
   const int K1 = q.p.K + 1;
-  if (J < 1 || J > K1 || a->out_target_stats) return SSD_ERR_INVALID_ARG;
+  if (J < 1 || J > K1 || a.out_target_stats) return SSD_ERR_INVALID_ARG;
+  if ((int64_t)q.p.B * K1 * q.p.nchunk > kMaxGrid) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+// The streaming part of an early-exit verification: positions 0 .. J-1 of
+// every sequence; the gate, decided once per sequence; then J .. K of the
+// sequences with no clear rejection below J.
+hipError_t launch_early_streams(const Plan& q, int32_t J, hipStream_t st) {
+  const int K1 = q.p.K + 1;
   const int64_t nch = q.p.nchunk;
-  if ((int64_t)q.p.B * K1 * nch > kMaxGrid) return SSD_ERR_UNSUPPORTED;
-  hipStream_t st = (hipStream_t)stream;
-  (void)hipGetLastError();
-  // positions 0 .. J-1 of every sequence; the gate, decided once per
-  // sequence; then J .. K of the sequences with no clear rejection below J;
-  // then the verification of each sequence
   Params p = q.p;
   p.early = 1;
   p.jlo = 0;
@@ -631,9 +631,62 @@ ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
     e = dispatch<LGate>(q.dt, q.al, (int64_t)p.B, pg, st);
     if (e == hipSuccess) e = dispatch<LVerifyGated>(q.dt, q.al, (int64_t)p.B * (K1 - J) * nch, pg, st);
   }
-  p.jn = 0;
+  return e;
+}
+
+// An early-exit verification: its streaming part, then the verification of
+// each sequence.
+hipError_t launch_verify_early(const Plan& q, int32_t J, hipStream_t st) {
+  hipError_t e = launch_early_streams(q, J, st);
+  Params p = q.p;
+  p.early = 1;
   if (e == hipSuccess) e = dispatch<LVerifySeq>(q.dt, q.al, q.g_tail, p, st);
-  return hip_status(e);
+  return e;
+}
+
+ssd_status ssd_verify_early(const ssd_verify_args* a, int32_t J, void* stream) {
+  if (!a) return SSD_ERR_INVALID_ARG;
+  Plan q;
+  ssd_status s = plan_verify(*a, q);
+  if (s != SSD_OK) return s;
+  s = check_early(q, *a, J);
+  if (s != SSD_OK) return s;
+  (void)hipGetLastError();
+  return hip_status(launch_verify_early(q, J, (hipStream_t)stream));
+}
+
+ssd_status ssd_round_early(const ssd_verify_args* v, const ssd_sample_args* s, int32_t J, void* stream) {
+  Plan qv, qs;
+  ssd_status e = plan_round(v, s, qv, qs);
+  if (e != SSD_OK) return e;
+  if (v) {
+    e = check_early(qv, *v, J);
+    if (e != SSD_OK) return e;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (!v) return hip_status(launch_sample(qs, st));
+  if (!s || qv.dt != qs.dt || qv.al != qs.al || qs.p.rows <= kTwoLaunchRows) {
+    // alone, with element types that cannot share a launch, or at small
+    // batches (where early exit saves less than its launches cost): in turn
+    hipError_t he = launch_verify_early(qv, J, st);
+    if (he == hipSuccess && s) he = launch_sample(qs, st);
+    return hip_status(he);
+  }
+  // the early-exit streaming part of round i; then the verification of each
+  // sequence beside round i+1's streaming pass; then its epilogue
+  hipError_t he = launch_early_streams(qv, J, st);
+  Params pv = qv.p;
+  pv.early = 1;
+  const int64_t nv = qv.g_tail;
+  if (he == hipSuccess) {
+    he = timed(SSD_OP_SAMPLE, [&](hipEvent_t e0, hipEvent_t e1) {
+      return e0 ? dispatch<LRoundMidT>(qv.dt, qv.al, nv + qs.g_stream, pv, qs.p, (int)nv, st, e0, e1)
+                : dispatch<LRoundMid>(qv.dt, qv.al, nv + qs.g_stream, pv, qs.p, (int)nv, st);
+    });
+  }
+  if (he == hipSuccess) he = dispatch<LSampleEpi>(qs.dt, qs.al, qs.g_tail, qs.p, st);
+  return hip_status(he);
 }
 
 ssd_status ssd_round(const ssd_verify_args* v, const ssd_sample_args* s, void* stream) {

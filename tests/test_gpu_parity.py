@@ -434,6 +434,51 @@ def test_round_step_matches_separate_calls(case):
     _say(f"round {case[:3]}: accepted {v_ref['accept_len'].tolist()} hits {c_ref[0].tolist()}")
 
 
+@pytest.mark.parametrize("case", [c for c in ROUND_CASES if c[0] * (c[1] + 1) > 256 or c[0] == 16],
+                         ids=lambda c: f"B{c[0]}K{c[1]}V{c[2]}{DTNAME[c[3]]}{DTNAME[c[4]]}")
+def test_round_early_matches_separate_calls(case):
+    """ssd_round_early (early-exit verification of round i beside sampling of
+    round i+1): accepted lengths, bonus, p_j(x_j) up to k* (NaN past it),
+    cache lookup, keys and every sampling output identical to
+    ssd_verify_early followed by ssd_saguaro_sample, for J = 1, 2 and K+1."""
+    import lossless_verify_sample_amd as ssd
+    B, K, V, dtv, dts, kind = case
+    cv = W.custom(B, K, V, dtv, T=0.9, F=4, C=0.5, kind=kind, draft_sd=0.8, F_out=4)
+    cs = W.custom(B, K, V, dts, T=0.9, F=4, C=0.5, kind=kind, draft_sd=0.8, F_out=4)
+    T = torch.full((B,), 0.9, device=DEV)
+    T[: max(1, B // 8)] = 0.0  # greedy sequences
+    Fk = ssd.fanout(32, K, 0.6, V)
+    t, d = W.logits(cv, 0, DEV)
+    _, d1 = W.logits(cs, 1, DEV)
+    pay = W.payload(cv, 32, 0, DEV)
+    c0 = ssd.Cache(Fk, B, K, DEV, payload=pay, miss_fill=True)
+    s0 = ssd.saguaro_sample(d, T, 4, 0.5, 11, F_out=4, cache=c0)
+    for J in sorted({1, min(2, K + 1), K + 1}):
+        def run(use_round):
+            c1 = ssd.Cache(Fk, B, K, DEV, payload=pay)
+            va = dict(target=t, draft=d, temperature=T, F=4, C=0.5, seed=11, tokens=s0["tokens"], draft_q=s0["q"],
+                      draft_stats=s0["stats"], draft_topf_idx=s0["topf_idx"], cache=c0)
+            sa = dict(draft=d1, temperature=T, F=4, C=0.5, seed=12, F_out=4, cache=c1)
+            if use_round:
+                v, s = ssd.round_step(va, sa, early_J=J)
+            else:
+                v = ssd.verify_early(**va, J=J)
+                s = ssd.saguaro_sample(**sa)
+            torch.cuda.synchronize()
+            return ({k: x.clone() for k, x in v.items() if x is not None}, {k: x.clone() for k, x in s.items()},
+                    [c0.hit.clone(), c0.slot.clone(), c0.tokens.clone(), c1.keys.clone()])
+
+        v_ref, s_ref, c_ref = run(False)
+        v_got, s_got, c_got = run(True)
+        for k in v_ref:
+            assert torch.equal(v_got[k].nan_to_num(-7.0), v_ref[k].nan_to_num(-7.0)), (J, k)
+        for k in s_ref:
+            assert torch.equal(s_got[k], s_ref[k]), (J, k)
+        for a_, b_ in zip(c_got, c_ref):
+            assert torch.equal(a_, b_), J
+        _say(f"round early {case[:3]} J={J}: accepted {v_ref['accept_len'].tolist()[:16]}")
+
+
 FBIG = [
     # B, K, V, dtype, T, F, C, F_out, kind, greedy_half: sigma over F > 8 entries (the radix
     # threshold), and (K+1) F > 256, where acceptance, residual and bonus read the draft top-F

@@ -339,3 +339,21 @@ def test_phase_read_is_off_in_the_ordinary_build(L):
     assert f(0, buf, -1) == 1
     assert f(0, buf, 8192 * 8 + 1) == 1
     assert f(0, buf, 8) == 2
+
+
+def test_round_early_rejects_bad_arguments(L):
+    """ssd_round_early: no call, J outside [1, K+1] and target statistics are
+    refused before any launch (fake pointers are never dereferenced)."""
+    import lossless_verify_sample_amd as ssd
+    P = ctypes.c_void_p(1 << 20)
+    f = L.ssd_round_early
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, None, 2, None) == 1
+    ws, ws2 = ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 25)
+    Q = ctypes.c_void_p(1 << 26)
+    v = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, None, None, ws, 1 << 24)
+    s = ssd._SampleArgs(P, 1, 2, 3, 100, 100, P, 2, 0.5, 2, 0, Q, Q, Q, Q, Q, None, ws2, 1 << 24)
+    assert f(ctypes.byref(v), ctypes.byref(s), 0, None) == 1  # J < 1
+    assert f(ctypes.byref(v), ctypes.byref(s), 5, None) == 1  # J > K + 1
+    vs = ssd._VerifyArgs(P, P, 1, 2, 3, 100, 100, P, 2, 0.5, 0, P, P, P, P, 2, P, P, P, P, None, ws, 1 << 24)
+    assert f(ctypes.byref(vs), ctypes.byref(s), 2, None) == 1  # target statistics
