@@ -113,7 +113,8 @@ struct Params {
   int32_t* acc_len;
   int32_t* bonus;
   float* p_out;
-  int32_t* alive;           // early exit: 1 when a sequence has no clear rejection below the gate [B]
+  int32_t* gate;            // early exit: [0] the number of sequences the gate keeps, [1 + i] the i-th of them [1 + B]
+  int gate_reset;           // verification stream: the first workgroup sets gate[0] to 0
   // speculation cache (optional): depth offsets, keys, payload, lookup outputs
   int koff[MAX_K1 + 1];
   int Bgt;
@@ -1574,6 +1575,9 @@ __device__ __forceinline__ void stream_item(const Params& p, int item) {
   if (lane == 0 && b0 < NB) p.part[row * NB + b0] = P0;
   if (lane == 0 && b1 < NB) p.part[row * NB + b1] = P1;
   if constexpr (MODE == M_VERIFY) {
+    if (p.gate_reset && item == 0 && threadIdx.x == 0) p.gate[0] = 0;
+  }
+  if constexpr (MODE == M_VERIFY) {
     // the workgroup whose chunk holds x_j hands its target logit to the epilogue
     if (xj >= 0 && xj < V && xj / (CH * BLK) == chunk && threadIdx.x == 0)
       p.zcap[(row / K1) * p.K + (row % K1)] = load_elem<DT>(rp, xj);
@@ -1655,22 +1659,28 @@ __device__ __forceinline__ bool seq_alive(const Params& p, int b, int J, GateSm&
 }
 
 // The early-exit gate, decided once per sequence (one workgroup each) over
-// the partials of positions 0 .. jlo - 1.
+// the partials of positions 0 .. jlo - 1: a kept sequence takes the next
+// place of the list (its order follows the atomics, which changes only which
+// workgroup streams which rows).
 template <int DT, bool AL>
 __global__ __launch_bounds__(EWG) void k_gate(Params p) {
   __shared__ GateSm g;
   const int b = blockIdx.x;
   const bool alive = p.NB <= 128 ? seq_alive<2>(p, b, p.jlo, g) : seq_alive<NBL>(p, b, p.jlo, g);
-  if (threadIdx.x == 0) p.alive[b] = alive ? 1 : 0;
+  if (alive && threadIdx.x == 0) p.gate[1 + atomicAdd(&p.gate[0], 1)] = b;
 }
 
-// Streaming pass of verification over positions jlo .. jlo + jn - 1, for the
-// sequences the gate kept (the others' workgroups return after one load).
+// Streaming pass of verification over positions jlo .. jlo + jn - 1 of the
+// sequences the gate kept: workgroup g streams item g % per of the
+// (g / per)-th listed sequence; workgroups past the list return (they come
+// last, so the kept rows fill the machine first).
 template <int DT, bool AL>
 __global__ __launch_bounds__(WG, (DT == SSD_F32 || !AL) ? 4 : 6) void k_stream_gated(Params p) {
-  const int b = (int)((blockIdx.x / p.nchunk) / p.jn);
-  if (!p.alive[b]) return;
-  stream_item<DT, AL, M_VERIFY>(p, blockIdx.x);
+  const int per = p.jn * p.nchunk;
+  const int k = (int)blockIdx.x / per;
+  const int n = p.gate[0], b = p.gate[1 + k];  // (both loads issued together; k < B)
+  if (k >= n) return;
+  stream_item<DT, AL, M_VERIFY>(p, b * per + (int)blockIdx.x % per);
 }
 
 // Sampling epilogue item g: row g, or (g >= rows) a long cache-key list.

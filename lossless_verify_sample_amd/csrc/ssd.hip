@@ -33,7 +33,7 @@ int64_t nblocks(int64_t V) { return (V + BLK - 1) / BLK; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-  size_t part, zcap, alive, total;
+  size_t part, zcap, gate, total;
 };
 
 // Workspace regions (256-byte aligned): block partials of every streamed row;
@@ -50,12 +50,12 @@ bool layout(ssd_op op, int64_t n, int32_t K, int64_t V, Layout* L) {
   const int64_t NB = nblocks(V);
   const int64_t rows = (op == SSD_OP_SAMPLE || op == SSD_OP_VERIFY || op == SSD_OP_VERIFY_TREE) ? n * (K + 1) : n;
   L->part = 0;
-  L->zcap = L->alive = 0;
+  L->zcap = L->gate = 0;
   size_t end = al256((size_t)(rows * NB) * sizeof(float4));
   if (op == SSD_OP_VERIFY) {
     L->zcap = end;
-    L->alive = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
-    end = L->alive + al256((size_t)n * sizeof(int32_t));
+    L->gate = L->zcap + al256((size_t)(n * (K > 0 ? K : 1)) * sizeof(float));
+    end = L->gate + al256((size_t)(n + 1) * sizeof(int32_t));
   }
   L->total = end;
   return true;
@@ -323,7 +323,7 @@ ssd_status plan_verify(const ssd_verify_args& a, Plan& q) {
   p.dtok = a.draft_tokens;
   p.dq = a.draft_q;
   p.zcap = (float*)(ws + L.zcap);
-  p.alive = (int32_t*)(ws + L.alive);
+  p.gate = (int32_t*)(ws + L.gate);
   p.dstats = a.draft_stats;
   p.dtopf = F > 0 ? a.draft_topf_idx : nullptr;
   p.ld_dtopf = a.ld_topf;
@@ -623,9 +623,11 @@ hipError_t launch_early_streams(const Plan& q, int32_t J, hipStream_t st) {
   p.early = 1;
   p.jlo = 0;
   p.jn = J;
+  p.gate_reset = 1;
   hipError_t e = dispatch<LVerify>(q.dt, q.al, (int64_t)p.B * J * nch, p, st);
   if (e == hipSuccess && J < K1) {
     Params pg = p;
+    pg.gate_reset = 0;
     pg.jlo = J;
     pg.jn = K1 - J;
     e = dispatch<LGate>(q.dt, q.al, (int64_t)p.B, pg, st);
