@@ -130,6 +130,13 @@ struct Params {
 };
 
 // LDS of an epilogue workgroup.
+// The top-F selection's plan, set by wave 0 for the workgroup: whether
+// candidate blocks are re-read, the one-element candidates listed, the
+// candidate and re-read block counts, the threshold.
+struct TopfQ {
+  int reread, n1, ncb, nrb;
+  float tau;
+};
 struct ESm {
   float rf[2][ENW];         // reduction slots, one per call site
   double rd[2][ENW];
@@ -142,6 +149,7 @@ struct ESm {
   uint64_t cand[CAND_CAP];  // top-F candidates as (value desc, index asc) keys
   uint64_t tkey[MAX_F];     // top-F result through LDS, sorted
   uint64_t wk[ENW][64];     // each wave's own top-F exchange row
+  TopfQ tq;                 // top-F plan (wave 0)
   int tf[TF_CAP];           // verification: the draft top-F lists of a sequence's rows
   int nre;                  // candidates appended by block re-reads
   int ks;
@@ -378,17 +386,21 @@ __device__ __forceinline__ uint32_t kth_key_rounds(const uint32_t (&key)[PLN], i
 // elements, so tau, the Fs-th largest of them, bounds the Fs-th largest
 // element from below, and every top element lies in a candidate block
 // (maximum >= tau).  A candidate whose second value is below tau holds
-// exactly one element >= tau, its maximum, whose index the partial carries.  When every
-// candidate is of that kind (the common case) each wave ranks the candidate
-// maxima itself; otherwise the other candidates are re-read by the whole
-// workgroup (each thread one 16-byte chunk of each) and all candidates are
-// ranked through LDS.  On return lane
-// r < Fs of every wave holds entry r as a (value, index) key, 0 elsewhere.
-// Every wave of the workgroup calls; sm.nre must have been cleared at start.
+// exactly one element >= tau, its maximum, whose index the partial carries.
+// When every candidate is of that kind (the common case) the wave ranks the
+// candidate maxima itself; otherwise the other candidates are re-read by the
+// whole workgroup (each thread one 16-byte chunk of each) and all candidates
+// are ranked through LDS.  sm.nre must have been cleared at start.
+//
+// topf_plan (one wave, or every wave with the same copy): tau and the
+// candidates.  In the common case it writes the ranked list to out[0 .. Fs)
+// and returns true; otherwise wave 0 lists the candidate blocks, the blocks
+// to re-read and the one-element candidates with the plan in sm.tq, and it
+// returns false.
 template <int DT, bool AL, int PLN>
-__device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, int NB, int Fs, const WRow<PLN>& r,
-                                              float m, ESm& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ bool topf_plan(int NB, int Fs, const WRow<PLN>& r, float m, ESm& sm, uint64_t* out) {
+  const int lane = threadIdx.x & 63;
+  const bool w0 = threadIdx.x < 64;
   // the block maxima and second values: 2 NB values of distinct elements
   // (a second value of -inf in a one-element block stands for none)
   uint32_t key[2 * PLN];
@@ -414,6 +426,7 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
     more |= __ballot(cand[i] && !one[i]);
   }
   if (more == 0) {
+    // every candidate holds one element >= tau: rank the candidate maxima
     uint64_t ck[PLN];
     int rk[PLN];
 #pragma unroll
@@ -431,38 +444,45 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
         for (int i2 = 0; i2 < PLN; ++i2) rk[i2] += kc > ck[i2];  // candidates ranked above
       }
     }
-    uint64_t* wk = sm.wk[wave];
 #pragma unroll
     for (int i = 0; i < PLN; ++i)
-      if (cand[i] && rk[i] < Fs) wk[rk[i]] = ck[i];
-    // lanes of one wave exchange through their own LDS rows: LDS executes a
-    // wave's accesses in order; the fences keep the compiler from reordering
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    return lane < Fs ? wk[lane] : 0ull;
-  }
-  // general case: wave 0 lists the candidate blocks, the blocks to re-read
-  // and the one-element candidates; then every thread scans its 16-byte
-  // chunks of the re-read blocks, RB blocks' loads in flight at a time
-  lds_sync();
-  const uint64_t below = (1ull << lane) - 1ull;
-  int n1 = 0, ncb = 0, nrb = 0;
+      if (cand[i] && rk[i] < Fs) out[rk[i]] = ck[i];
+    if (w0 && lane == 0) sm.tq.reread = 0;
+    return true;
+  } else {
+    // the candidate blocks, the blocks to re-read and the one-element
+    // candidates, listed for the whole workgroup
+    const uint64_t below = (1ull << lane) - 1ull;
+    int n1 = 0, ncb = 0, nrb = 0;
 #pragma unroll
-  for (int i = 0; i < PLN; ++i) {
-    const int be = lane + 64 * i;
-    const bool re = cand[i] && !one[i];
-    const uint64_t cm = __ballot(cand[i]), om = __ballot(one[i]), rm = __ballot(re);
-    if (wave == 0) {
-      if (cand[i]) sm.cblk[ncb + __popcll(cm & below)] = be;
-      if (re) sm.rblk[nrb + __popcll(rm & below)] = be;
-      if (one[i] && n1 + __popcll(om & below) < CAND_CAP) sm.cand[n1 + __popcll(om & below)] = vi_key(r.M[i], r.I[i]);
+    for (int i = 0; i < PLN; ++i) {
+      const int be = lane + 64 * i;
+      const bool re = cand[i] && !one[i];
+      const uint64_t cm = __ballot(cand[i]), om = __ballot(one[i]), rm = __ballot(re);
+      if (w0 && cand[i]) sm.cblk[ncb + __popcll(cm & below)] = be;
+      if (w0 && re) sm.rblk[nrb + __popcll(rm & below)] = be;
+      if (w0 && one[i] && n1 + __popcll(om & below) < CAND_CAP)
+        sm.cand[n1 + __popcll(om & below)] = vi_key(r.M[i], r.I[i]);
+      ncb += __popcll(cm);
+      n1 += __popcll(om);
+      nrb += __popcll(rm);
     }
-    ncb += __popcll(cm);
-    n1 += __popcll(om);
-    nrb += __popcll(rm);
+    if (w0 && lane == 0) sm.tq = TopfQ{1, n1, ncb, nrb, tau};
+    return false;
   }
-  lds_sync();
+}
+
+// The whole workgroup, after a barrier that follows topf_plan's false: every
+// thread scans its 16-byte chunks of the re-read blocks and all candidates
+// are ranked into sm.tkey; ends with a barrier.
+template <int DT, bool AL>
+__device__ __forceinline__ void topf_reread(const unsigned char* rp, int V, int Fs, ESm& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const TopfQ q = sm.tq;
+  // every thread scans its 16-byte chunks of the re-read blocks, RB blocks'
+  // loads in flight at a time
+  const float tau = q.tau;
+  const int n1 = q.n1, ncb = q.ncb, nrb = q.nrb;
   {
     constexpr int VW = Dt<DT>::VW, RB = 8;
     for (int c0 = tid; c0 < BLK / VW; c0 += EWG) {  // chunk c0 of every re-read block
@@ -547,6 +567,39 @@ __device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, in
     }
   }
   lds_sync();
+}
+
+// Every wave with its own copy of the partials: in the common case each
+// wave ranks the candidates itself and returns without a barrier (latency
+// first: the sampling epilogue's draw goes on in every wave).
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ uint64_t wave_topf(const unsigned char* rp, int V, int NB, int Fs, const WRow<PLN>& r,
+                                              float m, ESm& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t* wk = sm.wk[wave];
+  if (topf_plan<DT, AL, PLN>(NB, Fs, r, m, sm, wk)) {
+    // lanes of one wave exchange through their own LDS rows: LDS executes a
+    // wave's accesses in order; the fences keep the compiler from reordering
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return lane < Fs ? wk[lane] : 0ull;
+  }
+  lds_sync();
+  topf_reread<DT, AL>(rp, V, Fs, sm);
+  return lane < Fs ? sm.tkey[lane] : 0ull;
+}
+
+// Wave 0 alone plans the selection from its copy of the partials while the
+// other waves wait (throughput first: workgroups whose only output is the
+// list).
+template <int DT, bool AL, int PLN>
+__device__ __forceinline__ uint64_t wg_topf(const unsigned char* rp, int V, int NB, int Fs, const WRow<PLN>& r,
+                                            float m, ESm& sm) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) topf_plan<DT, AL, PLN>(NB, Fs, r, m, sm, sm.tkey);
+  lds_sync();
+  if (sm.tq.reread) topf_reread<DT, AL>(rp, V, Fs, sm);
   return lane < Fs ? sm.tkey[lane] : 0ull;
 }
 
@@ -725,12 +778,15 @@ __device__ __forceinline__ void epi_topf_p(const Params& p, int64_t row, ESm& sm
   if (threadIdx.x == 0) sm.nre = 0;
   const int NB = p.NB;
   WRow<PLN> r;
-  load_wrow<PLN>(p.part + row * NB, NB, r);
-  float lm = r.M[0];
+  float m = 0.f;
+  if (threadIdx.x < 64) {  // wave 0's copy of the partials serves the selection
+    load_wrow<PLN>(p.part + row * NB, NB, r);
+    float lm = r.M[0];
 #pragma unroll
-  for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
-  const float m = wave_max(lm);
-  const uint64_t tk = wave_topf<DT, AL, PLN>(p.x + row * p.ld * Dt<DT>::SZ, (int)p.V, NB, p.F, r, m, sm);
+    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+    m = wave_max(lm);
+  }
+  const uint64_t tk = wg_topf<DT, AL, PLN>(p.x + row * p.ld * Dt<DT>::SZ, (int)p.V, NB, p.F, r, m, sm);
   const int lane = threadIdx.x;
   if (lane < p.F) {  // wave 0 only: lane < F <= 64
     p.out_idx[row * p.F + lane] = (int)key_idx(tk);
@@ -886,12 +942,15 @@ __device__ __forceinline__ void epi_keys_p(const Params& p, int item, ESm& sm) {
   if (threadIdx.x == 0) sm.nre = 0;
   const int NB = p.NB;
   WRow<PLN> r;
-  load_wrow<PLN>(p.part + row * NB, NB, r);
-  float lm = r.M[0];
+  float m = 0.f;
+  if (threadIdx.x < 64) {  // wave 0's copy of the partials serves the selection
+    load_wrow<PLN>(p.part + row * NB, NB, r);
+    float lm = r.M[0];
 #pragma unroll
-  for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
-  const float m = wave_max(lm);
-  const uint64_t tk = wave_topf<DT, AL, PLN>(p.x + row * p.ld * Dt<DT>::SZ, (int)p.V, NB, Fj, r, m, sm);
+    for (int i = 1; i < PLN; ++i) lm = fmaxf(lm, r.M[i]);
+    m = wave_max(lm);
+  }
+  const uint64_t tk = wg_topf<DT, AL, PLN>(p.x + row * p.ld * Dt<DT>::SZ, (int)p.V, NB, Fj, r, m, sm);
   const int lane = threadIdx.x;
   if (lane < Fj) p.ckeys[(int64_t)b * p.Bgt + p.koff[j] + lane] = (int)key_idx(tk);  // wave 0: Fj <= 64
 }
