@@ -539,31 +539,93 @@ __device__ __forceinline__ void topf_reread(const unsigned char* rp, int V, int 
       if (rk < Fs) sm.tkey[rk] = ki;
     }
   } else {
-    // Many ties at the threshold: take the best key below the previous one,
-    // Fs times, over the candidate blocks (alternating reduction slots).
-    uint64_t prev = ~0ull;
+    // More than CAND_CAP elements at or above tau (a short row with a long
+    // list, or many ties): the Fs-th largest key by a radix select over the
+    // candidate blocks' elements, eight bits a round from the top (a 256-bin
+    // histogram in LDS of the keys that share the bits fixed so far), until
+    // the keys sharing the prefix are exactly the ones still needed; then
+    // those keys and every larger one (Fs in all) are collected and ranked.
     constexpr int VW = Dt<DT>::VW;
-    for (int rr = 0; rr < Fs; ++rr) {
-      uint64_t best = 0;
-      for (int c = wave; c < ncb; c += ENW) {
+    static_assert(EWG == 256, "one histogram bin per thread");
+    int* hist = reinterpret_cast<int*>(sm.cand);  // (the candidate list is not read here)
+    auto scan = [&](auto&& fn) {
+      for (int c = 0; c < ncb; ++c) {
         const int be = sm.cblk[c];
-#pragma unroll 1
-        for (int i = 0; i < 32 / VW; ++i) {
-          const int e0 = be * BLK + (i * 64 + lane) * VW;
+        for (int c0 = tid; c0 < BLK / VW; c0 += EWG) {
+          const int e0 = be * BLK + c0 * VW;
           float v[VW];
           load_chunk<DT, AL>(rp, V, e0, v);
 #pragma unroll
-          for (int e = 0; e < VW; ++e) {
-            if (v[e] >= tau && e0 + e < V) {
-              const uint64_t kk = vi_key(v[e], e0 + e);
-              if (kk < prev) best = umax64(best, kk);
-            }
-          }
+          for (int e = 0; e < VW; ++e)
+            if (v[e] >= tau && e0 + e < V) fn(vi_key(v[e], e0 + e));
         }
       }
-      best = wg_max_u64(best, sm.ru[4 + (rr & 1)]);
-      if (tid == 0) sm.tkey[rr] = best;
-      prev = best;
+    };
+    uint64_t prefix = 0, pmask = 0;
+    int need = Fs;
+    for (int sh = 56; sh >= 0; sh -= 8) {
+      hist[tid] = 0;
+      lds_sync();
+      scan([&](uint64_t k) {
+        if ((k & pmask) == prefix) atomicAdd(&hist[(int)(k >> sh) & 255], 1);
+      });
+      lds_sync();
+      if (wave == 0) {
+        // lane l holds bins 4l .. 4l+3; the need-th largest key of the
+        // prefix lies in the highest lane whose bins and those above reach
+        // need, in the highest of its bins that reaches it
+        int h[4], hs = 0;
+#pragma unroll
+        for (int b2 = 0; b2 < 4; ++b2) {
+          h[b2] = hist[4 * lane + b2];
+          hs += h[b2];
+        }
+        int suf = hs;  // bins of lanes >= l
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int t = __shfl_down(suf, off);
+          suf += lane + off < 64 ? t : 0;
+        }
+        const uint64_t reach = __ballot(suf >= need);
+        const int ls = 63 - (int)__builtin_clzll(reach);  // reach != 0: the prefix's keys number >= need
+        if (lane == ls) {
+          int cum = suf - hs, d = 4 * lane, hd = h[0];
+#pragma unroll
+          for (int b2 = 3; b2 >= 0; --b2) {
+            if (cum + h[b2] >= need) {
+              d = 4 * lane + b2;
+              hd = h[b2];
+              break;
+            }
+            cum += h[b2];
+          }
+          sm.ri[0][0] = d;
+          sm.ri[0][1] = cum;
+          sm.ri[0][2] = hd;
+        }
+      }
+      lds_sync();
+      const int d = sm.ri[0][0], above = sm.ri[0][1], hd = sm.ri[0][2];
+      need -= above;
+      prefix |= (uint64_t)d << sh;
+      pmask |= 255ull << sh;
+      if (hd == need) break;  // uniform: every thread read the same values
+    }
+    // the Fs keys: those above the prefix and those sharing it
+    if (tid == 0) sm.ri[1][0] = 0;
+    lds_sync();
+    scan([&](uint64_t k) {
+      if ((k & pmask) >= prefix) {
+        const int pos = atomicAdd(&sm.ri[1][0], 1);
+        if (pos < Fs) sm.cand[pos] = k;
+      }
+    });
+    lds_sync();
+    for (int c = tid; c < Fs; c += EWG) {
+      const uint64_t ki = sm.cand[c];
+      int rk = 0;
+      for (int c2 = 0; c2 < Fs; ++c2) rk += sm.cand[c2] > ki;
+      sm.tkey[rk] = ki;
     }
   }
   lds_sync();

@@ -128,6 +128,33 @@ def test_topf_tie_overflow_path():
         assert np.array_equal(val[r].cpu().numpy().astype(np.float64), ov)
 
 
+@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("V,F,kind", [(1000, 30, "normal"), (3000, 40, "normal"), (9000, 64, "int"),
+                                      (20000, 64, "few"), (2048, 17, "int")])
+def test_topf_long_lists_on_short_rows(dt, V, F, kind):
+    """More elements at or above the threshold than the candidate list holds
+    (lists longer than twice the block count, integer-valued rows with many
+    ties, rows of a few distinct values): the radix-select path, exact
+    against the oracle."""
+    import lossless_verify_sample_amd as ssd
+    from oracle import ssd as O
+    g = torch.Generator(device=DEV).manual_seed(V + F)
+    R = 3
+    x = torch.randn((R, V), generator=g, device=DEV) * 3
+    if kind == "int":
+        x = x.round()
+    elif kind == "few":
+        x = (x > 0).float() + (x > 2).float()
+    x = x.to(dt)
+    idx, val = ssd.topf(x, F)
+    torch.cuda.synchronize()
+    xr = O.decode(raw_host(x), DTNAME[dt])
+    for r in range(R):
+        oi, ov = O.topf(xr[r], F)
+        assert list(idx[r].cpu().numpy()) == list(oi), (V, F, kind, r)
+        assert np.array_equal(val[r].cpu().numpy().astype(np.float64), ov)
+
+
 @pytest.mark.parametrize("dt", [F32, BF16, F16])
 def test_softmax_t_and_probs(dt):
     import lossless_verify_sample_amd as ssd
