@@ -1270,12 +1270,14 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
   const int K = p.K, K1 = K + 1, NB = p.NB, tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = (int)p.V;
-  const float T = p.temp[b];
-  const bool greedy = !(T > 0.f);
-  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
-  const double invT = greedy ? 0.0 : 1.0 / (double)T;
   const int64_t r0 = (int64_t)b * K1;
   const int64_t rs = p.ld * Dt<DT>::SZ;
+  // the partials of this wave's first two rows are requested before anything
+  // else (every other load and the temperature's would otherwise go first,
+  // the temperature's round trip ahead of all of them)
+  WRow<PLN> ra, rb;
+  load_wrow<PLN>(p.part + (r0 + min(wave, K)) * NB, NB, ra);
+  load_wrow<PLN>(p.part + (r0 + min(wave + ENW, K)) * NB, NB, rb);
   // rows of up to 128 blocks (two per lane) keep their block values in LDS
   // when the K + 1 rows fit
   const bool fit = PLN <= 2 && K1 * NB <= PM_CAP;
@@ -1287,7 +1289,7 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
   // (the residual of row k* needs one); wave 0: the cache keys and payload.
   // All loaded unconditionally from clamped indices (a valid stand-in array
   // when K = 0 or F = 0: the captured-logit workspace), so that they and the
-  // partials below are in flight together (a load under a branch gets a wait
+  // partials above are in flight together (a load under a branch gets a wait
   // of its own) and no load waits on k*.
   const int F = p.F;
   const bool tf_lds = F > 0 && K1 * F <= TF_CAP;
@@ -1302,6 +1304,10 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
   const int tfv = *tfp;
   CacheRegs cr;
   cache_prefetch(p, b, cr);
+  const float T = p.temp[b];
+  const bool greedy = !(T > 0.f);
+  const float s = greedy ? 0.f : (float)(LOG2E / (double)T);
+  const double invT = greedy ? 0.0 : 1.0 / (double)T;
   const int xj = tid < K ? xl : -1;
   const float qj = tid < K ? ql : 0.f, ztj = tid < K ? zl : 0.f;
   const float dmax = (tid <= K && !greedy) ? ds.max : 0.f;
@@ -1374,9 +1380,10 @@ __device__ __forceinline__ void verify_seq(const Params& p, int b, VSm& sm) {
   int fbt = -1;
   for (int j0 = wave; j0 < K1; j0 += 2 * ENW) {
     const int j1 = j0 + ENW;
-    WRow<PLN> ra, rb;
-    load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
-    load_wrow<PLN>(p.part + (r0 + min(j1, K)) * NB, NB, rb);
+    if (j0 != wave) {  // (K + 1 > 2 ENW rows only)
+      load_wrow<PLN>(p.part + (r0 + j0) * NB, NB, ra);
+      load_wrow<PLN>(p.part + (r0 + min(j1, K)) * NB, NB, rb);
+    }
     // wave 0, lane j: the acceptance draw u_j and the fallback token j of a
     // cache miss, computed while the partials load
     if (wave == 0 && j0 == 0) {

@@ -37,6 +37,8 @@ SMALL = [
     (3, 2, 70001, BF16, 2.0, 0, 0.5, 0, "normal", False),   # F = 0, odd V
     (2, 2, 300000, BF16, 1.0, 4, 0.5, 27, "zipf", False),   # NB = 147 > 128: rows of 8 partials per lane
     (2, 1, 1 << 20, F16, 0.8, 4, 0.5, 8, "normal", True),   # the largest vocabulary (NB = 512)
+    (3, 11, 3000, BF16, 1.0, 4, 0.5, 4, "normal", False),   # K + 1 = 12 > 8 rows: a wave merges rows in two passes
+    (2, 32, 2500, F32, 0.8, 2, 0.5, 2, "peaks", True),      # K = 32, the largest, with a greedy sequence
 ]
 
 
@@ -254,6 +256,7 @@ EARLY = [
     (5, 2, 300000, BF16, 1.0, 4, 0.5, "zipf", False, 2),    # NB > 128
     (2, 0, 3000, BF16, 1.0, 2, 0.5, "normal", False, 1),    # K = 0
     (4, 3, 4099, F16, 1.1, 0, 1.0, "normal", True, 2),      # unaligned fp16, F = 0, C = 1, greedy half
+    (3, 11, 3000, BF16, 1.0, 4, 0.5, "normal", False, 3),   # K + 1 = 12 > 8 rows
 ]
 
 
