@@ -39,6 +39,8 @@ SMALL = [
     (2, 1, 1 << 20, F16, 0.8, 4, 0.5, 8, "normal", True),   # the largest vocabulary (NB = 512)
     (3, 11, 3000, BF16, 1.0, 4, 0.5, 4, "normal", False),   # K + 1 = 12 > 8 rows: a wave merges rows in two passes
     (2, 32, 2500, F32, 0.8, 2, 0.5, 2, "peaks", True),      # K = 32, the largest, with a greedy sequence
+    (3, 4, 20000, BF16, 0.02, 4, 0.5, 4, "normal", False),  # T = 0.02: nearly greedy, most blocks weigh 0
+    (3, 4, 20000, F32, 50.0, 4, 0.5, 4, "peaks", False),    # T = 50: nearly uniform, small residuals
 ]
 
 
